@@ -1,0 +1,156 @@
+/*
+ * moe.h -- C ABI of libmoe, the forward pass of one sparse mixture-of-experts
+ * (MoE) feed-forward layer on an AMD Instinct MI355X (gfx950).
+ *
+ * The layer (sources: the web pages "Mixture of Experts and Hybrid
+ * Architectures" (cheat sheet), "Mixture of experts and architecture
+ * families", "Sparse MoE FFN" (DeepSeek-V3) and "Lesson 2 -- From the Dense
+ * FFN to a Layer of Experts"):
+ *
+ *   l[t][e]  = u[t] . W_router[e]                      router, fp32 accumulate
+ *   s        = l            (MOE_SCORE_SOFTMAX)        select on raw scores
+ *            = sigmoid(l)   (MOE_SCORE_SIGMOID)        affinities
+ *   sb       = s + bias                                selection only
+ *   groups   : n_groups contiguous blocks of E/n_groups experts; group score
+ *              = sum of its two largest sb; keep the topk_groups best groups
+ *   topk_idx = the k largest sb among eligible experts, descending, ties to
+ *              the lower index; NaN ranks below every number
+ *   gates    = route_scale * softmax(l over the k chosen)      (SOFTMAX)
+ *            = route_scale * s / sum(s over the k chosen)      (SIGMOID)
+ *   y[t]     = sum_j gates[t][j] * FFN_{topk_idx[t][j]}(u[t]) + FFN_shared(u[t])
+ *   FFN(x)   = W2 (SiLU(W1 x) * W3 x),  SiLU(x) = x sigmoid(x)
+ *
+ * "The router in code" (cheat sheet) fixes selection on score + bias, the
+ * stable descending sort, and the softmax over the chosen raw scores.  "Sparse
+ * MoE FFN", "How it works" (Routing, eq. 12, Packed forward) fixes sigmoid
+ * affinities, group masking (8 groups keep 4, group score = sum of top-2),
+ * renormalised gates times route_scale 2.5, the SwiGLU expert, the always-on
+ * unweighted shared expert, and that no token is dropped.  The module returns
+ * shared + routed; the residual is added by the caller.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are device memory owned by the caller, row-major and
+ *     contiguous, 16-byte aligned.  The library never allocates device memory
+ *     and keeps no state between calls (except the optional timing records).
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL for
+ *     the default stream); calls return after enqueueing and never
+ *     synchronise.  Device faults surface at the caller's next sync.
+ *   - Arguments are validated before anything is launched.  On a negative
+ *     status nothing was launched and no output was written.
+ *   - T == 0 is a valid no-op.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,      /* a required pointer is NULL                      */
+    MOE_ERR_SHAPE = -2,     /* a size is out of the supported range            */
+    MOE_ERR_CFG = -3,       /* inconsistent routing configuration              */
+    MOE_ERR_DTYPE = -4,     /* unknown dtype or score function                 */
+    MOE_ERR_WORKSPACE = -5, /* workspace missing or smaller than required      */
+    MOE_ERR_HIP = -6,       /* a HIP launch or runtime call failed             */
+    MOE_ERR_ALIGN = -7      /* a pointer is not 16-byte aligned                */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
+
+typedef struct {
+    int64_t T;           /* tokens (rows of u), >= 0                               */
+    int32_t d;           /* hidden size, multiple of 64                            */
+    int32_t E;           /* routed experts, 1..256                                 */
+    int32_t k;           /* experts per token, 1..min(E, 32)                       */
+    int32_t F;           /* routed expert inner width, multiple of 64              */
+    int32_t F_shared;    /* shared expert inner width (N_s * F fused), 0 = none    */
+    int32_t dtype;       /* moe_dtype of u, y and every weight matrix              */
+    int32_t score_fn;    /* moe_score_fn                                           */
+    int32_t n_groups;    /* expert groups (1 = no group limit); divides E, <= 64   */
+    int32_t topk_groups; /* groups kept per token, 1..n_groups                     */
+    float route_scale;   /* gate multiplier: 1.0 for softmax, 2.5 for DeepSeek-V3  */
+} moe_cfg;
+
+/* Shared (always-on) expert weights: W1, W3 [F_shared][d], W2 [d][F_shared]. */
+typedef struct {
+    const void *W1;
+    const void *W3;
+    const void *W2;
+} moe_shared;
+
+/* Bytes of device workspace moe_layer_forward and moe_route_debug need for
+ * cfg, or 0 when cfg is invalid.  The buffer is scratch: its contents on
+ * entry do not matter and are overwritten. */
+size_t moe_workspace_bytes(const moe_cfg *cfg);
+
+/* Checks cfg without touching the GPU; MOE_OK or the status the entry points
+ * would return for it. */
+moe_status moe_check_cfg(const moe_cfg *cfg);
+
+/*
+ * The whole layer forward.
+ *   u        [T][d]       cfg->dtype   token inputs (pre-normed by the caller)
+ *   W_router [E][d]       cfg->dtype   router rows e_i
+ *   bias     [E]          fp32         selection-only bias; NULL == all zeros
+ *   W1, W3   [E][F][d]    cfg->dtype   expert gate / up projections
+ *   W2       [E][d][F]    cfg->dtype   expert down projections
+ *   shared   NULL == no shared expert (then cfg->F_shared must be 0)
+ *   y        [T][d]       cfg->dtype   out: shared + routed (no residual);
+ *                                      overwritten, must not alias u
+ *   topk_idx [T][k]       int32        out: chosen experts, descending sb
+ *   gates    [T][k]       fp32         out: gate of each chosen expert
+ *   workspace, workspace_bytes          >= moe_workspace_bytes(cfg)
+ * Internally: fp32 accumulation everywhere; for bf16 the SwiGLU activations
+ * and the per-slot expert outputs are stored as bf16 and y is rounded to
+ * bf16 (nearest even).  The result is bitwise deterministic: there are no
+ * floating-point atomics.
+ */
+moe_status moe_layer_forward(const void *u, const void *W_router, const float *bias,
+                             const void *W1, const void *W3, const void *W2,
+                             const moe_shared *shared, const moe_cfg *cfg, void *y,
+                             int32_t *topk_idx, float *gates, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * Routing and permutation only (the first two stages of moe_layer_forward,
+ * same kernels), for tests and tools.  Outputs, all int32 device arrays:
+ *   counts [E]       slots that chose expert e
+ *   offsets [E+1]    exclusive prefix sum of counts; offsets[E] = T*k
+ *   perm [T*k]       slot (t*k + j) at each expert-contiguous position; within
+ *                    an expert, slots ascend (stable)
+ *   inv [T*k]        position of each slot
+ * Any of counts/offsets/perm/inv may be NULL (not copied out).
+ */
+moe_status moe_route_debug(const void *u, const void *W_router, const float *bias,
+                           const moe_cfg *cfg, int32_t *topk_idx, float *gates,
+                           int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable text of a status code (static storage). */
+const char *moe_status_str(int status);
+
+/*
+ * Optional per-stage GPU timing.  While enabled, every moe_layer_forward call
+ * records a HIP event before and after each stage on its stream.
+ * moe_timing_read synchronises on the recorded events, adds the elapsed
+ * milliseconds of each stage into ms[MOE_N_STAGES], stores the number of
+ * calls measured in *calls, and (reset != 0) clears the records.
+ * Stages: 0 router+top-k, 1 permutation, 2 gate/up projections with SiLU*mul,
+ * 3 down projections, 4 gate-weighted combine.
+ */
+#define MOE_N_STAGES 5
+moe_status moe_timing_enable(int on);
+moe_status moe_timing_read(double *ms, int64_t *calls, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

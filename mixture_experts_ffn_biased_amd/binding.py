@@ -1,0 +1,239 @@
+"""ctypes binding of libmoe (include/moe.h), with the same entry-point names.
+
+Argument marshalling only: checks that tensors have the shapes, dtypes and
+device the ABI expects, allocates outputs and workspace with torch, and passes
+raw device pointers plus torch's current HIP stream.  Every step of the layer
+runs in the library's HIP kernels; if ``libmoe.so`` is missing this module
+raises instead of computing anything another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_N_STAGES = 5
+STAGES = ("router_topk", "permute", "gate_up", "down", "combine")
+
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_CFG",
+          -4: "MOE_ERR_DTYPE", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP", -7: "MOE_ERR_ALIGN"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({moe_status_str(status)})")
+
+
+class moe_cfg(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("F", ctypes.c_int32), ("F_shared", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("score_fn", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32),
+                ("route_scale", ctypes.c_float)]
+
+
+class moe_shared(ctypes.Structure):
+    _fields_ = [("W1", ctypes.c_void_p), ("W3", ctypes.c_void_p), ("W2", ctypes.c_void_p)]
+
+
+@dataclass(frozen=True)
+class MoeConfig:
+    """Python mirror of moe_cfg."""
+    T: int
+    d: int
+    E: int
+    k: int
+    F: int
+    F_shared: int = 0
+    dtype: str = "bf16"          # "bf16" | "f32"
+    score_fn: str = "softmax"    # "softmax" | "sigmoid"
+    n_groups: int = 1
+    topk_groups: int = 1
+    route_scale: float = 1.0
+
+    def to_c(self) -> moe_cfg:
+        return moe_cfg(self.T, self.d, self.E, self.k, self.F, self.F_shared,
+                       MOE_BF16 if self.dtype == "bf16" else
+                       (MOE_F32 if self.dtype == "f32" else 99),
+                       MOE_SCORE_SIGMOID if self.score_fn == "sigmoid" else
+                       (MOE_SCORE_SOFTMAX if self.score_fn == "softmax" else 99),
+                       self.n_groups, self.topk_groups, self.route_scale)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    @classmethod
+    def from_workload(cls, w, T: Optional[int] = None) -> "MoeConfig":
+        return cls(T=w.T if T is None else T, d=w.d, E=w.E, k=w.k, F=w.F, F_shared=w.Fs,
+                   dtype=w.dtype, score_fn=w.score_fn, n_groups=w.n_groups,
+                   topk_groups=w.topk_groups, route_scale=w.route_scale)
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoe.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_ffn_biased_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        CP = ctypes.POINTER(moe_cfg)
+        L.moe_workspace_bytes.argtypes = [CP]
+        L.moe_workspace_bytes.restype = SZ
+        L.moe_check_cfg.argtypes = [CP]
+        L.moe_check_cfg.restype = I32
+        L.moe_layer_forward.argtypes = [P, P, P, P, P, P, ctypes.POINTER(moe_shared), CP, P, P, P,
+                                        P, SZ, P]
+        L.moe_layer_forward.restype = I32
+        L.moe_route_debug.argtypes = [P, P, P, CP, P, P, P, P, P, P, P, SZ, P]
+        L.moe_route_debug.restype = I32
+        L.moe_status_str.argtypes = [I32]
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_timing_enable.argtypes = [I32]
+        L.moe_timing_enable.restype = I32
+        L.moe_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]
+        L.moe_timing_read.restype = I32
+        _lib = L
+    return _lib
+
+
+def moe_status_str(status: int) -> str:
+    return lib().moe_status_str(int(status)).decode()
+
+
+def moe_check_cfg(cfg: MoeConfig) -> int:
+    c = cfg.to_c()
+    return int(lib().moe_check_cfg(ctypes.byref(c)))
+
+
+def moe_workspace_bytes(cfg: MoeConfig) -> int:
+    c = cfg.to_c()
+    return int(lib().moe_workspace_bytes(ctypes.byref(c)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, shape, dtype, name, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, is on {t.device}")
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def alloc_workspace(cfg: MoeConfig, device) -> torch.Tensor:
+    n = moe_workspace_bytes(cfg)
+    if n == 0 and cfg.T > 0:
+        raise MoeError(moe_check_cfg(cfg), "moe_workspace_bytes")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_layer_forward(u, W_router, bias, W1, W3, W2, shared: Optional[Sequence] = None, *,
+                      cfg: MoeConfig, y=None, topk_idx=None, gates=None, workspace=None,
+                      stream=None):
+    """y, topk_idx, gates = moe_layer_forward(u, W_router, bias, W1, W3, W2, shared, cfg=cfg).
+
+    shared: None or (W1s [Fs][d], W3s [Fs][d], W2s [d][Fs]).  bias: fp32 [E] or None."""
+    dev = u.device
+    dt = cfg.torch_dtype
+    T, d, E, k, F, Fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.F_shared
+    _need(u, (T, d), dt, "u", dev)
+    _need(W_router, (E, d), dt, "W_router", dev)
+    _need(W1, (E, F, d), dt, "W1", dev)
+    _need(W3, (E, F, d), dt, "W3", dev)
+    _need(W2, (E, d, F), dt, "W2", dev)
+    if bias is not None:
+        _need(bias, (E,), torch.float32, "bias", dev)
+    sh = None
+    if shared is not None:
+        W1s, W3s, W2s = shared
+        _need(W1s, (Fs, d), dt, "W1s", dev)
+        _need(W3s, (Fs, d), dt, "W3s", dev)
+        _need(W2s, (d, Fs), dt, "W2s", dev)
+        sh = moe_shared(W1s.data_ptr(), W3s.data_ptr(), W2s.data_ptr())
+    if y is None:
+        y = torch.empty((T, d), dtype=dt, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if gates is None:
+        gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(y, (T, d), dt, "y", dev)
+    _need(topk_idx, (T, k), torch.int32, "topk_idx", dev)
+    _need(gates, (T, k), torch.float32, "gates", dev)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, dev)
+    c = cfg.to_c()
+    st = lib().moe_layer_forward(_ptr(u), _ptr(W_router), _ptr(bias), _ptr(W1), _ptr(W3), _ptr(W2),
+                                 ctypes.byref(sh) if sh is not None else None, ctypes.byref(c),
+                                 _ptr(y), _ptr(topk_idx), _ptr(gates), _ptr(workspace),
+                                 workspace.numel(), _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_layer_forward")
+    return y, topk_idx, gates
+
+
+def moe_route_debug(u, W_router, bias, *, cfg: MoeConfig, workspace=None, stream=None):
+    """Routing + permutation only: (topk_idx, gates, counts, offsets, perm, inv)."""
+    dev = u.device
+    dt = cfg.torch_dtype
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    _need(u, (T, d), dt, "u", dev)
+    _need(W_router, (E, d), dt, "W_router", dev)
+    if bias is not None:
+        _need(bias, (E,), torch.float32, "bias", dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    topk_idx = torch.empty((T, k), **i32)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, **i32)
+    offsets = torch.empty(E + 1, **i32)
+    perm = torch.empty(T * k, **i32)
+    inv = torch.empty(T * k, **i32)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, dev)
+    c = cfg.to_c()
+    st = lib().moe_route_debug(_ptr(u), _ptr(W_router), _ptr(bias), ctypes.byref(c),
+                               _ptr(topk_idx), _ptr(gates), _ptr(counts), _ptr(offsets),
+                               _ptr(perm), _ptr(inv), _ptr(workspace), workspace.numel(),
+                               _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_route_debug")
+    return topk_idx, gates, counts, offsets, perm, inv
+
+
+def moe_timing_enable(on: bool) -> None:
+    lib().moe_timing_enable(1 if on else 0)
+
+
+def moe_timing_read(reset: bool = True):
+    """(milliseconds per stage summed over the recorded calls, number of calls)."""
+    ms = (ctypes.c_double * MOE_N_STAGES)()
+    calls = ctypes.c_int64(0)
+    st = lib().moe_timing_read(ms, ctypes.byref(calls), 1 if reset else 0)
+    if st != 0:
+        raise MoeError(st, "moe_timing_read")
+    return list(ms), int(calls.value)

@@ -1,0 +1,101 @@
+// Stage 5: gate-weighted combine, y[t] = Z[t] + sum_j gates[t][j] * O[inv[t*k+j]].
+//
+// "Sparse MoE FFN" (DeepSeek-V3), eq. 12 and "Packed forward": the routed
+// outputs are scaled by their gates and summed, the shared output is added
+// unweighted, and every token receives all k routed outputs (no dropping).
+// Instead of a scatter-add into a zero buffer, each token reads its k rows
+// through the inverse permutation and sums them in a fixed order with fp32
+// accumulation: no atomics, bitwise deterministic.
+#include "common.hpp"
+#include "plan.hpp"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__ O,
+                                                    const float *__restrict__ Z,
+                                                    const int32_t *__restrict__ inv,
+                                                    const float *__restrict__ gates, int64_t T,
+                                                    int d, int k, uint16_t *__restrict__ y) {
+  const int64_t t = blockIdx.x;
+  const int nchunk = d / 8;
+  __shared__ int pos[kMaxTopK];
+  __shared__ float gw[kMaxTopK];
+  if (threadIdx.x < k) {
+    pos[threadIdx.x] = inv[t * k + threadIdx.x];
+    gw[threadIdx.x] = gates[t * k + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < nchunk; c += 256) {
+    float acc[8];
+    if (Z) {
+      const float4 z0 = *reinterpret_cast<const float4 *>(Z + t * d + c * 8);
+      const float4 z1 = *reinterpret_cast<const float4 *>(Z + t * d + c * 8 + 4);
+      acc[0] = z0.x; acc[1] = z0.y; acc[2] = z0.z; acc[3] = z0.w;
+      acc[4] = z1.x; acc[5] = z1.y; acc[6] = z1.z; acc[7] = z1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    }
+    for (int j = 0; j < k; ++j) {
+      const uint4 o = *reinterpret_cast<const uint4 *>(O + static_cast<int64_t>(pos[j]) * d + c * 8);
+      const float g = gw[j];
+      const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(g, bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu)), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(g, bf16_to_f32(static_cast<uint16_t>(w[i] >> 16)), acc[2 * i + 1]);
+      }
+    }
+    uint4 out;
+    out.x = pack_bf16x2(acc[0], acc[1]);
+    out.y = pack_bf16x2(acc[2], acc[3]);
+    out.z = pack_bf16x2(acc[4], acc[5]);
+    out.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4 *>(y + t * d + c * 8) = out;
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_f32(const float *__restrict__ O,
+                                                   const float *__restrict__ Z,
+                                                   const int32_t *__restrict__ inv,
+                                                   const float *__restrict__ gates, int64_t T, int d,
+                                                   int k, float *__restrict__ y) {
+  const int64_t t = blockIdx.x;
+  __shared__ int pos[kMaxTopK];
+  __shared__ float gw[kMaxTopK];
+  if (threadIdx.x < k) {
+    pos[threadIdx.x] = inv[t * k + threadIdx.x];
+    gw[threadIdx.x] = gates[t * k + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < d / 4; c += 256) {
+    float4 acc = Z ? *reinterpret_cast<const float4 *>(Z + t * d + c * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const float4 o = *reinterpret_cast<const float4 *>(O + static_cast<int64_t>(pos[j]) * d + c * 4);
+      const float g = gw[j];
+      acc.x = fmaf(g, o.x, acc.x);
+      acc.y = fmaf(g, o.y, acc.y);
+      acc.z = fmaf(g, o.z, acc.z);
+      acc.w = fmaf(g, o.w, acc.w);
+    }
+    *reinterpret_cast<float4 *>(y + t * d + c * 4) = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Plan &p, const float *gates, void *y, hipStream_t s) {
+  const moe_cfg &c = p.cfg;
+  const float *Z = c.F_shared > 0 ? p.Z : nullptr;
+  const dim3 grid(static_cast<unsigned>(c.T));
+  if (c.dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_bf16, grid, dim3(256), 0, s, static_cast<const uint16_t *>(p.O), Z,
+                       p.inv, gates, c.T, c.d, c.k, static_cast<uint16_t *>(y));
+  else
+    hipLaunchKernelGGL(combine_f32, grid, dim3(256), 0, s, static_cast<const float *>(p.O), Z, p.inv,
+                       gates, c.T, c.d, c.k, static_cast<float *>(y));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,81 @@
+// Shared device helpers for the gfx950 MoE kernels: bf16 bit handling, vector
+// types, the wave64 MFMA fragment types and an order key for top-k.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 is the upper half of an IEEE binary32.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+// Total order used by top-k: larger score first, then lower index; NaN ranks
+// below every number; -0 and +0 tie.  The 64-bit key is compared as an
+// unsigned integer; 0 is reserved for "no candidate".
+__device__ __forceinline__ uint64_t rank_key(float v, int idx) {
+  uint32_t k;
+  if (v != v) {
+    k = 0u;
+  } else {
+    uint32_t b = __float_as_uint(v + 0.0f);  // -0 -> +0
+    k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  }
+  return (static_cast<uint64_t>(k) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(idx));
+}
+
+__device__ __forceinline__ int key_index(uint64_t key) {
+  return static_cast<int>(~static_cast<uint32_t>(key & 0xffffffffu));
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  uint32_t k = static_cast<uint32_t>(key >> 32);
+  if (k == 0u) return __uint_as_float(0x7fc00000u);
+  uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(b);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  lo = __shfl_xor(lo, mask, 64);
+  hi = __shfl_xor(hi, mask, 64);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Butterfly maximum over the 64 lanes of a wave; every lane gets the result.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+}  // namespace moe

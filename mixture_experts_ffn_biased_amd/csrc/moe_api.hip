@@ -1,0 +1,242 @@
+// The C ABI of libmoe (declared in include/moe.h): validation, workspace
+// carve-up, the five-stage launch sequence and optional per-stage timing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "plan.hpp"
+
+namespace moe {
+
+int gemm_tile_m(int dtype);
+
+moe_status validate(const moe_cfg *c) {
+  if (!c) return MOE_ERR_NULL;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_DTYPE;
+  if (c->T < 0) return MOE_ERR_SHAPE;
+  if (c->d <= 0 || c->d % 64 != 0) return MOE_ERR_SHAPE;
+  if (c->F <= 0 || c->F % 64 != 0) return MOE_ERR_SHAPE;
+  if (c->F_shared < 0 || c->F_shared % 64 != 0) return MOE_ERR_SHAPE;
+  if (c->E < 1 || c->E > kMaxExperts) return MOE_ERR_SHAPE;
+  if (c->k < 1 || c->k > c->E || c->k > kMaxTopK) return MOE_ERR_CFG;
+  if (c->n_groups < 1 || c->n_groups > kMaxGroups || c->E % c->n_groups != 0) return MOE_ERR_CFG;
+  if (c->topk_groups < 1 || c->topk_groups > c->n_groups) return MOE_ERR_CFG;
+  if (c->n_groups > 1) {
+    const int per = c->E / c->n_groups;
+    if (per < 2 || c->k > c->topk_groups * per) return MOE_ERR_CFG;
+  }
+  if (!std::isfinite(c->route_scale)) return MOE_ERR_CFG;
+  if (c->T * static_cast<int64_t>(c->k) > 0x7fffffffLL - 1024) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+static size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+void make_plan(const moe_cfg &c, void *base, Plan *p) {
+  p->cfg = c;
+  p->S = c.T * c.k;
+  p->tile_m = gemm_tile_m(c.dtype);
+  p->n_perm_blocks = (p->S + kPermChunk - 1) / kPermChunk;
+  p->max_tiles = (p->S + p->tile_m - 1) / p->tile_m + c.E +
+                 (c.F_shared > 0 ? (c.T + p->tile_m - 1) / p->tile_m : 0);
+  const size_t es = c.dtype == MOE_BF16 ? 2 : 4;
+  char *b = static_cast<char *>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void * {
+    void *ptr = b ? b + off : nullptr;
+    off += align_up(bytes);
+    return ptr;
+  };
+  p->blk_counts = static_cast<int32_t *>(take(sizeof(int32_t) * p->n_perm_blocks * c.E));
+  p->blk_base = static_cast<int32_t *>(take(sizeof(int32_t) * p->n_perm_blocks * c.E));
+  p->counts = static_cast<int32_t *>(take(sizeof(int32_t) * c.E));
+  p->offsets = static_cast<int32_t *>(take(sizeof(int32_t) * (c.E + 1)));
+  p->perm = static_cast<int32_t *>(take(sizeof(int32_t) * p->S));
+  p->inv = static_cast<int32_t *>(take(sizeof(int32_t) * p->S));
+  p->tiles = static_cast<Tile *>(take(sizeof(Tile) * p->max_tiles));
+  p->tile_count = static_cast<int32_t *>(take(sizeof(int32_t)));
+  p->H = take(es * p->S * c.F);
+  p->Hs = take(es * c.T * c.F_shared);
+  p->O = take(es * p->S * c.d);
+  p->Z = static_cast<float *>(take(c.F_shared > 0 ? sizeof(float) * c.T * c.d : 0));
+  p->bytes = off;
+}
+
+// ---- optional per-stage timing ----------------------------------------------
+
+namespace {
+struct Record {
+  hipEvent_t ev[MOE_N_STAGES + 1];
+};
+std::mutex g_mu;
+bool g_timing = false;
+std::vector<Record> g_records;
+constexpr size_t kMaxRecords = 100000;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+}  // namespace
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_cfg *cfg) {
+  if (validate(cfg) != MOE_OK) return 0;
+  Plan p;
+  make_plan(*cfg, nullptr, &p);
+  return p.bytes;
+}
+
+moe_status moe_check_cfg(const moe_cfg *cfg) { return validate(cfg); }
+
+const char *moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of the supported range";
+    case MOE_ERR_CFG: return "inconsistent routing configuration";
+    case MOE_ERR_DTYPE: return "unknown dtype or score function";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+    case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+static moe_status prepare(const moe_cfg *cfg, void *workspace, size_t workspace_bytes, Plan *p) {
+  Plan probe;
+  make_plan(*cfg, nullptr, &probe);
+  if (!workspace) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes < probe.bytes) return MOE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+  make_plan(*cfg, workspace, p);
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(const void *u, const void *W_router, const float *bias, const void *W1,
+                             const void *W3, const void *W2, const moe_shared *shared,
+                             const moe_cfg *cfg, void *y, int32_t *topk_idx, float *gates,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if ((cfg->F_shared > 0) != (shared != nullptr)) return MOE_ERR_CFG;
+  if (cfg->T == 0) return MOE_OK;
+  if (!u || !W_router || !W1 || !W3 || !W2 || !y || !topk_idx || !gates) return MOE_ERR_NULL;
+  if (shared && (!shared->W1 || !shared->W3 || !shared->W2)) return MOE_ERR_NULL;
+  const void *ptrs[] = {u, W_router, W1, W3, W2, y, shared ? shared->W1 : u,
+                        shared ? shared->W3 : u, shared ? shared->W2 : u};
+  for (const void *q : ptrs)
+    if (!aligned16(q)) return MOE_ERR_ALIGN;
+  {
+    const size_t bytes = static_cast<size_t>(cfg->T) * cfg->d * (cfg->dtype == MOE_BF16 ? 2 : 4);
+    const char *a = static_cast<const char *>(u);
+    const char *b = static_cast<const char *>(y);
+    if (a < b + bytes && b < a + bytes) return MOE_ERR_SHAPE;  // y aliases u
+  }
+  Plan p;
+  st = prepare(cfg, workspace, workspace_bytes, &p);
+  if (st != MOE_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // report only errors of the launches below
+
+  Record rec{};
+  bool timed = false;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_timing && g_records.size() < kMaxRecords) {
+      timed = true;
+      for (auto &e : rec.ev)
+        if (hipEventCreate(&e) != hipSuccess) return MOE_ERR_HIP;
+    }
+  }
+  auto mark = [&](int i) {
+    if (timed) (void)hipEventRecord(rec.ev[i], s);
+  };
+
+  mark(0);
+  if (launch_router_topk(p, u, W_router, bias, topk_idx, gates, s) != hipSuccess) return MOE_ERR_HIP;
+  mark(1);
+  if (launch_permute(p, topk_idx, s) != hipSuccess) return MOE_ERR_HIP;
+  mark(2);
+  if (launch_gate_up(p, u, W1, W3, shared ? shared->W1 : nullptr, shared ? shared->W3 : nullptr, s) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  mark(3);
+  if (launch_down(p, W2, shared ? shared->W2 : nullptr, s) != hipSuccess) return MOE_ERR_HIP;
+  mark(4);
+  if (launch_combine(p, gates, y, s) != hipSuccess) return MOE_ERR_HIP;
+  mark(5);
+  if (timed) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_records.push_back(rec);
+  }
+  return MOE_OK;
+}
+
+moe_status moe_route_debug(const void *u, const void *W_router, const float *bias, const moe_cfg *cfg,
+                           int32_t *topk_idx, float *gates, int32_t *counts, int32_t *offsets,
+                           int32_t *perm, int32_t *inv, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+  moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!u || !W_router || !topk_idx || !gates) return MOE_ERR_NULL;
+  if (!aligned16(u) || !aligned16(W_router)) return MOE_ERR_ALIGN;
+  Plan p;
+  st = prepare(cfg, workspace, workspace_bytes, &p);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (launch_router_topk(p, u, W_router, bias, topk_idx, gates, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_permute(p, topk_idx, s) != hipSuccess) return MOE_ERR_HIP;
+  const int E = cfg->E;
+  if (counts && hipMemcpyAsync(counts, p.counts, sizeof(int32_t) * E, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (offsets &&
+      hipMemcpyAsync(offsets, p.offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (perm && hipMemcpyAsync(perm, p.perm, sizeof(int32_t) * p.S, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (inv && hipMemcpyAsync(inv, p.inv, sizeof(int32_t) * p.S, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_timing = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_timing_read(double *ms, int64_t *calls, int reset) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (ms)
+    for (int i = 0; i < MOE_N_STAGES; ++i) ms[i] = 0.0;
+  moe_status st = MOE_OK;
+  for (auto &r : g_records) {
+    if (hipEventSynchronize(r.ev[MOE_N_STAGES]) != hipSuccess) {
+      st = MOE_ERR_HIP;
+      continue;
+    }
+    for (int i = 0; i < MOE_N_STAGES; ++i) {
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, r.ev[i], r.ev[i + 1]) != hipSuccess) st = MOE_ERR_HIP;
+      if (ms) ms[i] += t;
+    }
+  }
+  if (calls) *calls = static_cast<int64_t>(g_records.size());
+  if (reset) {
+    for (auto &r : g_records)
+      for (auto &e : r.ev) (void)hipEventDestroy(e);
+    g_records.clear();
+  }
+  return st;
+}
+
+}  // extern "C"

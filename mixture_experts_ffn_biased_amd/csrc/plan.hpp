@@ -1,0 +1,62 @@
+// Host-side plan of one layer call: validated sizes, the carve-up of the
+// caller's workspace, and the launchers of the five stages.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// One row block of the grouped GEMMs: `nrows` consecutive rows starting at
+// row `row0` of expert `group` (group == E: the shared expert, whose rows are
+// the tokens themselves).
+struct Tile {
+  int32_t group;
+  int32_t row0;
+  int32_t nrows;
+  int32_t pad;
+};
+
+constexpr int kPermChunk = 1024;  // slots per block in the permutation kernels
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxGroups = 64;
+
+struct Plan {
+  moe_cfg cfg;
+  int64_t S;        // routed slots, T*k
+  int tile_m;       // rows per grouped-GEMM tile
+  int64_t n_perm_blocks;
+  int64_t max_tiles;
+  // workspace carve-up (device pointers; null when only sizing)
+  int32_t *blk_counts;  // [n_perm_blocks][E]
+  int32_t *blk_base;    // [n_perm_blocks][E]
+  int32_t *counts;      // [E]
+  int32_t *offsets;     // [E+1]
+  int32_t *perm;        // [S]  slot at each expert-contiguous position
+  int32_t *inv;         // [S]  position of each slot
+  Tile *tiles;          // [max_tiles]
+  int32_t *tile_count;  // [1]
+  void *H;              // [S][F]        SiLU(W1 x) * W3 x of each routed slot
+  void *Hs;             // [T][F_shared] same for the shared expert
+  void *O;              // [S][d]        expert output of each routed slot
+  float *Z;             // [T][d]        shared expert output (fp32)
+  size_t bytes;
+};
+
+moe_status validate(const moe_cfg *c);
+// Fills *p; base == nullptr computes only the size.
+void make_plan(const moe_cfg &c, void *base, Plan *p);
+
+hipError_t launch_router_topk(const Plan &p, const void *u, const void *Wr, const float *bias,
+                              int32_t *topk_idx, float *gates, hipStream_t s);
+hipError_t launch_permute(const Plan &p, const int32_t *topk_idx, hipStream_t s);
+hipError_t launch_gate_up(const Plan &p, const void *u, const void *W1, const void *W3,
+                          const void *W1s, const void *W3s, hipStream_t s);
+hipError_t launch_down(const Plan &p, const void *W2, const void *W2s, hipStream_t s);
+hipError_t launch_combine(const Plan &p, const float *gates, void *y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,260 @@
+// Stage 1: router GEMM fused with the score function, the selection-only
+// bias, the group limit and top-k, one wave per token for the selection.
+//
+// Router: l = u . W_router^T with fp32 accumulation ("Mixture of Experts and
+// Hybrid Architectures", "The router in code"; "Sparse MoE FFN", Routing:
+// u_t^T e_i).  bf16 inputs use the bf16 MFMA (products of bf16 values are
+// exact in fp32); fp32 inputs use fp32 FMA.
+//
+// Selection ("The router in code"; "Sparse MoE FFN", "How it works",
+// Routing): s = l (softmax mode) or sigmoid(l); sb = s + bias; with groups,
+// group score = sum of the two largest sb, keep the topk_groups best groups;
+// top-k of sb over eligible experts, larger first, ties to the lower index,
+// NaN last.  Gates come from the raw scores: softmax over the chosen logits,
+// or s / sum(s) over the chosen, times route_scale.
+#include "common.hpp"
+#include "plan.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kRows = 32;           // tokens per block
+constexpr int kLogitStride = 257;   // floats per logits row in LDS
+
+// LDS tile of rows x 64 bf16 (128 bytes a row) in 16-byte chunks, XOR
+// swizzled so that 16 consecutive rows reading one chunk hit distinct banks.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+struct SelArgs {
+  int E, k, score_fn, G, M;
+  float route_scale;
+  const float *bias;
+};
+
+// Selection for one token by one wave; lg = the token's E logits (LDS).
+__device__ void select_token(const float *lg, const SelArgs &a, int32_t *idx_out,
+                             float *gate_out) {
+  const int lane = threadIdx.x & 63;
+  constexpr int P = kMaxExperts / 64;
+  float gs[P];       // raw score used by the gates (l or sigmoid(l))
+  uint64_t key[P];   // ranking key of s + bias; 0 = not a candidate
+  int grp[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int e = lane + 64 * p;
+    gs[p] = 0.f;
+    key[p] = 0;
+    grp[p] = 0;
+    if (e < a.E) {
+      const float l = lg[e];
+      const float s = a.score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-l)) : l;
+      const float sb = s + (a.bias ? a.bias[e] : 0.0f);
+      gs[p] = s;
+      key[p] = rank_key(sb, e);
+      grp[p] = e / (a.E / a.G);
+    }
+  }
+
+  if (a.G > 1) {
+    // Group score: the two largest biased scores of each group.
+    float my_gscore = 0.f;
+    for (int g = 0; g < a.G; ++g) {
+      uint64_t k1 = 0;
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        if (grp[p] == g && key[p] > k1) k1 = key[p];
+      k1 = wave_max_u64(k1);
+      uint64_t k2 = 0;
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        if (grp[p] == g && key[p] != k1 && key[p] > k2) k2 = key[p];
+      k2 = wave_max_u64(k2);
+      const float sc = key_value(k1) + key_value(k2);
+      if (lane == g) my_gscore = sc;
+    }
+    uint64_t gkey = lane < a.G ? rank_key(my_gscore, lane) : 0;
+    uint64_t kept = 0;
+    for (int r = 0; r < a.M; ++r) {
+      const uint64_t best = wave_max_u64(gkey);
+      const int g = key_index(best);
+      kept |= 1ull << g;
+      if (lane == g) gkey = 0;
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (!((kept >> grp[p]) & 1ull)) key[p] = 0;
+  }
+
+  int my_idx = 0;
+  float my_gs = 0.f;
+  for (int j = 0; j < a.k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) best = key[p] > best ? key[p] : best;
+    best = wave_max_u64(best);
+    const int e = key_index(best);
+    const int owner = e & 63, pe = e >> 6;
+    float v = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (p == pe) v = gs[p];
+    v = __shfl(v, owner, 64);
+    if (lane == owner) {
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        if (p == pe) key[p] = 0;
+    }
+    if (lane == j) {
+      my_idx = e;
+      my_gs = v;
+    }
+  }
+
+  const bool mine = lane < a.k;
+  float gate;
+  if (a.score_fn == MOE_SCORE_SIGMOID) {
+    const float sum = wave_sum_f32(mine ? my_gs : 0.f);
+    gate = a.route_scale * my_gs / sum;
+  } else {
+    float m = mine ? my_gs : -INFINITY;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    const float ex = mine ? expf(my_gs - m) : 0.f;
+    const float sum = wave_sum_f32(ex);
+    gate = a.route_scale * ex / sum;
+  }
+  if (mine) {
+    idx_out[lane] = my_idx;
+    gate_out[lane] = gate;
+  }
+}
+
+__global__ __launch_bounds__(256) void router_topk_bf16(
+    const uint16_t *__restrict__ u, const uint16_t *__restrict__ Wr, int64_t T, int d,
+    SelArgs sel, int32_t *__restrict__ topk_idx, float *__restrict__ gates) {
+  // 32 x 64 bf16 A tile + 256 x 64 bf16 B tile; later reused for the logits.
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kRows * 128 + kMaxExperts * 128 + 256];
+  unsigned char *As = smem;
+  unsigned char *Bs = smem + kRows * 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRows;
+  const int E = sel.E;
+
+  const int lrow = tid >> 3, lch = tid & 7;
+  const int64_t at = t0 + lrow;
+  const uint16_t *arow = at < T ? u + at * d + lch * 8 : nullptr;
+  uint4 ra;
+  uint4 rb[kMaxExperts / 32];
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+
+  auto load = [&](int k0) {
+    ra = arow ? *reinterpret_cast<const uint4 *>(arow + k0) : zero;
+#pragma unroll
+    for (int i = 0; i < kMaxExperts / 32; ++i) {
+      const int e = lrow + 32 * i;
+      rb[i] = e < E ? *reinterpret_cast<const uint4 *>(Wr + static_cast<int64_t>(e) * d + k0 + lch * 8)
+                    : zero;
+    }
+  };
+  auto store = [&]() {
+    *reinterpret_cast<uint4 *>(As + swz(lrow, lch)) = ra;
+#pragma unroll
+    for (int i = 0; i < kMaxExperts / 32; ++i)
+      *reinterpret_cast<uint4 *>(Bs + swz(lrow + 32 * i, lch)) = rb[i];
+  };
+
+  const bool active = wave * 64 < E;
+  f32x16 acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  load(0);
+  store();
+  __syncthreads();
+  for (int k0 = 0; k0 < d; k0 += 64) {
+    const bool more = k0 + 64 < d;
+    if (more) load(k0 + 64);
+    if (active) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ch = kk * 2 + (lane >> 5);
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(As + swz(lane & 31, ch));
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const bf16x8 b = *reinterpret_cast<const bf16x8 *>(Bs + swz(wave * 64 + ni * 32 + (lane & 31), ch));
+          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[ni], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+    if (more) {
+      store();
+      __syncthreads();
+    }
+  }
+
+  float *lg = reinterpret_cast<float *>(smem);
+  if (active) {
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = wave * 64 + ni * 32 + (lane & 31);
+        if (col < E) lg[row * kLogitStride + col] = acc[ni][r];
+      }
+  }
+  __syncthreads();
+  for (int row = wave; row < kRows; row += 4) {
+    const int64_t t = t0 + row;
+    if (t >= T) break;
+    select_token(lg + row * kLogitStride, sel, topk_idx + t * sel.k, gates + t * sel.k);
+  }
+}
+
+__global__ __launch_bounds__(256) void router_topk_f32(
+    const float *__restrict__ u, const float *__restrict__ Wr, int64_t T, int d, SelArgs sel,
+    int32_t *__restrict__ topk_idx, float *__restrict__ gates) {
+  __shared__ float lg[kRows * kLogitStride];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRows;
+  const int E = sel.E;
+  for (int q = tid; q < kRows * E; q += 256) {
+    const int row = q / E, e = q % E;
+    const int64_t t = t0 + row;
+    if (t >= T) continue;
+    const float *x = u + t * d;
+    const float *w = Wr + static_cast<int64_t>(e) * d;
+    float acc = 0.f;
+    for (int j = 0; j < d; ++j) acc = fmaf(x[j], w[j], acc);
+    lg[row * kLogitStride + e] = acc;
+  }
+  __syncthreads();
+  for (int row = wave; row < kRows; row += 4) {
+    const int64_t t = t0 + row;
+    if (t >= T) break;
+    select_token(lg + row * kLogitStride, sel, topk_idx + t * sel.k, gates + t * sel.k);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_topk(const Plan &p, const void *u, const void *Wr, const float *bias,
+                              int32_t *topk_idx, float *gates, hipStream_t s) {
+  const moe_cfg &c = p.cfg;
+  SelArgs sel{c.E, c.k, c.score_fn, c.n_groups, c.topk_groups, c.route_scale, bias};
+  const dim3 grid(static_cast<unsigned>((c.T + kRows - 1) / kRows));
+  if (c.dtype == MOE_BF16)
+    hipLaunchKernelGGL(router_topk_bf16, grid, dim3(256), 0, s, static_cast<const uint16_t *>(u),
+                       static_cast<const uint16_t *>(Wr), c.T, c.d, sel, topk_idx, gates);
+  else
+    hipLaunchKernelGGL(router_topk_f32, grid, dim3(256), 0, s, static_cast<const float *>(u),
+                       static_cast<const float *>(Wr), c.T, c.d, sel, topk_idx, gates);
+  return hipGetLastError();
+}
+
+}  // namespace moe

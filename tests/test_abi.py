@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/moe.h declares, its struct layout matches the header,
+and invalid arguments are rejected before anything reaches the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+import torch
+
+import mixture_experts_ffn_biased_amd as moe
+from mixture_experts_ffn_biased_amd import binding
+from synthetic import WORKLOADS, make_inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"moe_layer_forward", "moe_workspace_bytes", "moe_route_debug",
+            "moe_status_str"} <= set(names)
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_[a-z_]+)", out))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(moe_cfg),"
+        " offsetof(moe_cfg, d), offsetof(moe_cfg, dtype), offsetof(moe_cfg, n_groups),"
+        " offsetof(moe_cfg, route_scale), sizeof(moe_shared)); return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    c = binding.moe_cfg
+    assert got == [ctypes.sizeof(c), c.d.offset, c.dtype.offset, c.n_groups.offset,
+                   c.route_scale.offset, ctypes.sizeof(binding.moe_shared)]
+
+
+def cfg(**kw):
+    base = dict(T=64, d=128, E=16, k=4, F=128, F_shared=0, dtype="bf16", score_fn="sigmoid",
+                n_groups=4, topk_groups=2, route_scale=2.5)
+    base.update(kw)
+    return moe.MoeConfig(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    ({"d": 100}, -2), ({"F": 96}, -2), ({"F_shared": 32}, -2), ({"E": 0}, -2), ({"E": 257}, -2),
+    ({"T": -1}, -2), ({"k": 0}, -3), ({"k": 17}, -3), ({"n_groups": 3}, -3),
+    ({"n_groups": 16}, -3), ({"topk_groups": 5}, -3), ({"k": 9}, -3),
+    ({"dtype": "fp8"}, -4), ({"score_fn": "relu"}, -4), ({"route_scale": float("nan")}, -3),
+    ({"n_groups": 1, "topk_groups": 1, "k": 16, "E": 16}, 0),
+    ({"E": 256, "n_groups": 8, "topk_groups": 4, "k": 8}, 0),
+])
+def test_config_validation(kw, status):
+    c = cfg(**kw)
+    assert moe.moe_check_cfg(c) == status
+    assert (moe.moe_workspace_bytes(c) > 0) == (status == 0)
+
+
+def test_workspace_grows_with_tokens_and_shared_expert():
+    a = moe.moe_workspace_bytes(cfg(T=64))
+    b = moe.moe_workspace_bytes(cfg(T=128))
+    c = moe.moe_workspace_bytes(cfg(T=128, F_shared=128))
+    assert 0 < a < b < c
+    for w in WORKLOADS.values():
+        assert moe.moe_workspace_bytes(moe.MoeConfig.from_workload(w)) > 0
+
+
+def _call(c, **ptrs):
+    """moe_layer_forward with fake (never dereferenced) aligned pointers."""
+    L = moe.lib()
+    p = {n: ctypes.c_void_p(0x10000 * (i + 1)) for i, n in enumerate(
+        ["u", "Wr", "W1", "W3", "W2", "y", "idx", "gates", "ws"])}
+    p.update(ptrs)
+    cc = c.to_c()
+    return L.moe_layer_forward(p["u"], p["Wr"], None, p["W1"], p["W3"], p["W2"], None,
+                               ctypes.byref(cc), p["y"], p["idx"], p["gates"], p["ws"],
+                               ptrs.get("ws_bytes", 16), None)
+
+
+def test_argument_errors_are_reported_before_any_launch():
+    c = cfg(n_groups=1, topk_groups=1)
+    assert _call(c, u=None) == -1
+    assert _call(c, ws=None) == -5
+    assert _call(c) == -5                      # workspace of 16 bytes is too small
+    assert _call(c, u=ctypes.c_void_p(0x10008)) == -7
+    assert _call(cfg(T=0)) == 0                # no-op
+    assert _call(cfg(F_shared=128)) == -3      # shared width given but no shared weights
+    assert _call(c, y=ctypes.c_void_p(0x10000)) == -2  # y aliases u
+    assert "workspace" in moe.moe_status_str(-5)
+
+
+def test_seeded_inputs_are_deterministic():
+    w = WORKLOADS["tiny_fp32"]
+    a = make_inputs(w, seed=3)
+    b = make_inputs(w, seed=3)
+    c = make_inputs(w, seed=4)
+    for k in ("u", "W_router", "W1", "W3", "W2", "bias"):
+        assert torch.equal(a[k], b[k])
+    assert not torch.equal(a["u"], c["u"])
+    assert a["W1"].dtype == torch.float32
+    w2 = WORKLOADS["dsv3_decode"].with_(E=8, n_groups=4, topk_groups=2, F=64, Fs=64, d=64)
+    x = make_inputs(w2, seed=0)
+    assert x["W1"].dtype == torch.bfloat16 and x["bias"].abs().max() <= 0.05
+    std = x["W1"].float().std().item()
+    assert abs(std - 1 / 8) < 0.02  # 1/sqrt(d)

@@ -1,0 +1,270 @@
+"""GPU parity of the HIP layer against the CPU oracle (through the C ABI).
+
+Small layers are checked on every token; the full-size workloads are checked
+on every token's routing and on a sample of tokens' outputs, in the same
+launch configuration the benchmark times.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_biased_amd as moe
+import oracle
+from oracle import balance, skew
+from parity import (Y_TOL, host, mode_of, oracle_inputs, rel_l2, route_parity, sampled_outputs,
+                    widen_gpu)
+from synthetic import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.lib()  # fails loudly when libmoe.so is missing
+    return torch.device("cuda:0")
+
+
+def run(w, inp, bias="given", **kw):
+    cfg = moe.MoeConfig.from_workload(w)
+    b = inp["bias"] if bias == "given" else bias
+    y, idx, g = moe.moe_layer_forward(inp["u"], inp["W_router"], b, inp["W1"], inp["W3"],
+                                      inp["W2"], inp["shared"], cfg=cfg, **kw)
+    torch.cuda.synchronize()
+    return y, idx, g
+
+
+def to_dev(inp, dev):
+    out = {}
+    for k_, v in inp.items():
+        if v is None:
+            out[k_] = None
+        elif isinstance(v, tuple):
+            out[k_] = tuple(t.to(dev) for t in v)
+        else:
+            out[k_] = v.to(dev)
+    return out
+
+
+def full_oracle(w, inp, forced=None):
+    u, Wr, bias = oracle_inputs(inp)
+    shared = None if inp["shared"] is None else tuple(host(t) for t in inp["shared"])
+    return oracle.forward(u, Wr, host(inp["W1"]), host(inp["W3"]), host(inp["W2"]), w.k,
+                          bias=bias, shared=shared, score_fn=mode_of(w), n_groups=w.n_groups,
+                          topk_groups=w.topk_groups, route_scale=w.route_scale,
+                          forced_idx=forced)
+
+
+def check_full(w, inp, y, idx, g):
+    """Every token: routing and output against the oracle."""
+    yr, ir, gr, ge, gg = full_oracle(w, inp)
+    u, Wr, bias = oracle_inputs(inp)
+    lg = oracle.router_logits(u, Wr)
+    gi = idx.cpu().numpy()
+    st = route_parity(w, gi, g.cpu().numpy(), ir, gr, ge, gg, lg, bias)
+    diff = ~(np.sort(gi, 1) == np.sort(ir, 1)).all(1)
+    if diff.any():  # near-ties the GPU broke the other way: oracle with its choice
+        t = np.nonzero(diff)[0]
+        shared = None if inp["shared"] is None else tuple(host(s) for s in inp["shared"])
+        sub = oracle.forward(u[t], Wr, host(inp["W1"]), host(inp["W3"]), host(inp["W2"]), w.k,
+                             shared=shared, score_fn=mode_of(w), route_scale=w.route_scale,
+                             n_groups=w.n_groups, topk_groups=w.topk_groups, forced_idx=gi[t])
+        yr[t] = sub[0]
+    err = rel_l2(widen_gpu(y), yr)
+    assert err.max() <= Y_TOL[w.dtype], f"max rel-L2 {err.max():.3e} at token {err.argmax()}"
+    st["rel_l2_max"] = float(err.max())
+    return st
+
+
+SMALL = {
+    "tiny_fp32": WORKLOADS["tiny_fp32"],
+    "sigmoid_groups_shared_bf16": Workload("sigmoid_groups_shared_bf16", 333, 256, 16, 4, 192, 128,
+                                           "sigmoid", 4, 2, 2.5, "bf16", "uniform"),
+    "softmax_bias_bf16": Workload("softmax_bias_bf16", 517, 192, 32, 6, 320, 0, "softmax", 1, 1,
+                                  1.0, "bf16", "uniform"),
+    "sigmoid_groups_fp32": Workload("sigmoid_groups_fp32", 200, 128, 16, 3, 128, 64, "sigmoid", 4,
+                                    2, 2.5, "f32", "uniform"),
+    "k_equals_E_bf16": Workload("k_equals_E_bf16", 70, 128, 8, 8, 128, 64, "softmax", 1, 1, 1.0,
+                                "bf16", "zero"),
+    "single_token_k1_bf16": Workload("single_token_k1_bf16", 1, 128, 4, 1, 64, 0, "softmax", 1, 1,
+                                     1.0, "bf16", "uniform"),
+    "e256_groups_bf16": Workload("e256_groups_bf16", 150, 128, 256, 8, 64, 64, "sigmoid", 8, 4, 2.5,
+                                 "bf16", "uniform"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layer_every_token(dev, name):
+    w = SMALL[name]
+    log(f"[small] {name}")
+    inp = to_dev(make_inputs(w, seed=1, device="cpu"), dev)
+    y, idx, g = run(w, inp)
+    st = check_full(w, inp, y, idx, g)
+    log(f"[small] {name} {st}")
+
+
+def test_one_expert_takes_every_token(dev):
+    """A large bias on expert 3 puts it in every token's set: one expert with
+    all T rows over several tiles, while the gate still uses the raw score."""
+    w = Workload("forced_e3", 300, 128, 8, 2, 128, 64, "softmax", 1, 1, 1.0, "bf16", "zero")
+    b = torch.zeros(8)
+    b[3] = 100.0
+    inp = to_dev(make_inputs(w, seed=2, device="cpu", bias=b), dev)
+    y, idx, g = run(w, inp)
+    assert (idx[:, 0] == 3).all()
+    check_full(w, inp, y, idx, g)
+
+
+def test_null_bias_is_bitwise_zero_bias_and_runs_are_deterministic(dev):
+    w = SMALL["sigmoid_groups_shared_bf16"].with_(bias="zero")
+    inp = to_dev(make_inputs(w, seed=3, device="cpu"), dev)
+    ref = run(w, inp)
+    none = run(w, inp, bias=None)
+    for a, b in zip(ref, none):
+        assert torch.equal(a, b)
+    for _ in range(3):
+        again = run(w, inp)
+        for a, b in zip(ref, again):
+            assert torch.equal(a, b)
+
+
+def test_nan_row_gives_valid_distinct_indices(dev):
+    w = SMALL["sigmoid_groups_shared_bf16"]
+    inp = make_inputs(w, seed=4, device="cpu")
+    inp["u"][7] = float("nan")
+    inp = to_dev(inp, dev)
+    y, idx, g = run(w, inp)
+    u, Wr, bias = oracle_inputs(inp)
+    ir, _, _, _, _ = oracle.route(u, Wr, w.k, mode_of(w), w.n_groups, w.topk_groups,
+                                  w.route_scale, bias=bias)
+    gi = idx.cpu().numpy()
+    assert ((gi >= 0) & (gi < w.E)).all()
+    assert len(set(gi[7].tolist())) == w.k
+    assert gi[7].tolist() == ir[7].tolist()
+
+
+def test_zero_tokens_is_a_noop(dev):
+    w = SMALL["softmax_bias_bf16"]
+    inp = to_dev(make_inputs(w.with_(T=4), seed=5, device="cpu"), dev)
+    cfg = moe.MoeConfig.from_workload(w, T=0)
+    u0 = inp["u"][:0]
+    y, idx, g = moe.moe_layer_forward(u0, inp["W_router"], inp["bias"], inp["W1"], inp["W3"],
+                                      inp["W2"], None, cfg=cfg)
+    assert y.shape == (0, w.d) and idx.shape == (0, w.k)
+
+
+@pytest.mark.parametrize("name", ["sigmoid_groups_shared_bf16", "e256_groups_bf16"])
+def test_route_debug_permutation_is_exact(dev, name):
+    w = SMALL[name].with_(T=3001)
+    inp = to_dev(make_inputs(w, seed=6, device="cpu"), dev)
+    cfg = moe.MoeConfig.from_workload(w)
+    idx, g, counts, offsets, perm, inv = moe.moe_route_debug(inp["u"], inp["W_router"],
+                                                             inp["bias"], cfg=cfg)
+    torch.cuda.synchronize()
+    c, o, p, iv = oracle.permutation(idx.cpu().numpy(), w.E)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(perm.cpu().numpy(), p)
+    assert np.array_equal(inv.cpu().numpy(), iv)
+    # routing of the debug entry point is the forward's routing
+    y2, idx2, g2 = run(w, inp)
+    assert torch.equal(idx, idx2) and torch.equal(g, g2)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def check_large(w, inp, n_sample, seed=0, must_include=None):
+    u, Wr, bias = oracle_inputs(inp)
+    bias_arg = bias if inp["bias"] is not None else None
+    log(f"[{w.name}] gpu forward")
+    y, idx, g = run(w, inp)
+    log(f"[{w.name}] oracle routing on {w.T} tokens")
+    ir, gr, ge, gg, lg = oracle.route(u, Wr, w.k, mode_of(w), w.n_groups, w.topk_groups,
+                                      w.route_scale, bias=bias_arg)
+    gi = idx.cpu().numpy()
+    st = route_parity(w, gi, g.cpu().numpy(), ir, gr, ge, gg, lg, bias)
+    rng = np.random.default_rng(seed)
+    tok = rng.choice(w.T, size=min(n_sample, w.T), replace=False)
+    if must_include is not None:
+        tok = np.unique(np.concatenate([tok, must_include]))
+    near = (ge < 1e-5) | (gg < 1e-5)
+    sel = np.where(near[tok, None], gi[tok], ir[tok])
+    log(f"[{w.name}] oracle outputs on {tok.size} tokens")
+    yr, _, _ = sampled_outputs(w, inp, tok, sel)
+    err = rel_l2(widen_gpu(y[torch.from_numpy(tok).to(y.device)]), yr)
+    assert err.max() <= Y_TOL[w.dtype], f"max rel-L2 {err.max():.3e}"
+    st["rel_l2_max"] = float(err.max())
+    st["sampled"] = int(tok.size)
+    log(f"[{w.name}] {st}")
+    return y, idx, g, st
+
+
+@pytest.fixture(autouse=True)
+def _release_memory():
+    yield
+    if torch.cuda.is_available():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def test_mixtral_full_size(dev):
+    w = WORKLOADS["mixtral_e8_top2"]
+    inp = make_inputs(w, seed=0, device=dev)
+    check_large(w, inp, n_sample=24)
+    del inp
+
+
+def test_dsv3_prefill_full_size(dev):
+    w = WORKLOADS["dsv3_prefill"]
+    inp = make_inputs(w, seed=0, device=dev)
+    check_large(w, inp, n_sample=12)
+    del inp
+
+
+def test_dsv3_decode_full_size(dev):
+    w = WORKLOADS["dsv3_decode"]
+    inp = make_inputs(w, seed=0, device=dev)
+    check_large(w, inp, n_sample=24)
+    del inp
+
+
+def test_skewed_load_bias_off_and_on(dev):
+    w = WORKLOADS["skewed_e128_top8"]
+    base = make_inputs(w, seed=0, device=dev)
+    u = host(base["u"])
+    Wr = host(base["W_router"])
+    lg = oracle.router_logits(u, Wr)
+    a = oracle.widen(u) @ base["skew_dir"].double().cpu().numpy()
+    alpha = skew.calibrate_expert0_scale(lg[:, 1:], a, w.k, target=0.90)
+    del base
+    inp = make_inputs(w, seed=0, device=dev, expert0_scale=alpha)
+    u, Wr, _ = oracle_inputs(inp)
+    lg = oracle.router_logits(u, Wr)
+    idx0, _, _, _ = oracle.select(lg, w.k, oracle.SOFTMAX)
+    share = float((idx0 == 0).any(1).mean())
+    log(f"[skewed] alpha={alpha:.4f} expert-0 share at zero bias={share:.4f}")
+    assert abs(share - 0.90) <= 0.005
+    # bias off
+    _, idx, _, st0 = check_large(w, inp, n_sample=16,
+                                 must_include=np.nonzero((idx0 == 0).any(1))[0][:8])
+    cnt0 = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.E)
+    # bias on: the aux-loss-free loop's correction vector
+    b, hist = balance.balance_bias(lg, w.k)
+    inp["bias"] = torch.from_numpy(b.astype(np.float32)).to(dev)
+    _, idx, _, st1 = check_large(w, inp, n_sample=16,
+                                 must_include=np.nonzero((idx0 == 0).any(1))[0][:8])
+    cnt1 = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.E)
+    e0, e1 = balance.entropy(cnt0), balance.entropy(cnt1)
+    log(f"[skewed] expert-0 rows {cnt0[0]} -> {cnt1[0]}, entropy {e0:.4f} -> {e1:.4f} "
+        f"(ln E = {math.log(w.E):.4f})")
+    assert cnt1[0] < cnt0[0] and e1 > e0
+    del inp
