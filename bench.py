@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE feed-forward layer forward on one MI355X.
+
+One step = one call of moe_layer_forward over the DeepSeek-V3-shaped prefill
+layer (T=8192 tokens, d=7168, 256 routed experts top-8 with sigmoid scores,
+8 groups keep 4, selection-only bias, route_scale 2.5, 1 shared expert,
+expert width 2048, bf16 with fp32 accumulation): router + top-k, permutation,
+gate/up + SiLU*mul, down, combine.  Inputs are seeded synthetic tensors,
+resident in HBM before the timed region starts.
+
+Printed: one JSON line with tokens/s, the layer's TFLOP/s and fraction of the
+bf16 MFMA peak, the roofline of the dominant kernel (gate/up, from HIP events
+recorded by the library on the launch stream during the timed steps), the
+decode-shaped layer (T=64, same weights) with its HBM bandwidth, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + % bf16 MFMA peak (DSv3 shape); decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0       # MI355X published HBM3E bandwidth
+GATE_UP = 2                 # stage index of the gate/up grouped GEMM
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--decode-workload", default="dsv3_decode")
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
+                    help="tokens whose expert outputs the CPU oracle computes")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    p = os.path.join(ROOT, "mixture_experts_ffn_biased_amd", "csrc", "grouped_gemm.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current source of the kernel; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("source_sha") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def timed_steps(step, steps, warmup, torch):
+    import mixture_experts_ffn_biased_amd as moe
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    moe.moe_timing_read(reset=True)
+    moe.moe_timing_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    moe.moe_timing_enable(False)
+    stage_ms, calls = moe.moe_timing_read(reset=True)
+    ms = e0.elapsed_time(e1) / steps
+    return ms, wall, [s / max(calls, 1) for s in stage_ms], calls
+
+
+def run_layer(w, inp, u, steps, warmup, torch):
+    import mixture_experts_ffn_biased_amd as moe
+    cfg = moe.MoeConfig.from_workload(w)
+    dev = u.device
+    y = torch.empty((w.T, w.d), dtype=u.dtype, device=dev)
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    gates = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    ws = moe.alloc_workspace(cfg, dev)
+
+    def step():
+        moe.moe_layer_forward(u, inp["W_router"], inp["bias"], inp["W1"], inp["W3"], inp["W2"],
+                              inp["shared"], cfg=cfg, y=y, topk_idx=idx, gates=gates,
+                              workspace=ws)
+
+    ms, wall, stage_ms, calls = timed_steps(step, steps, warmup, torch)
+    return ms, wall, stage_ms, idx
+
+
+def cpu_baseline(w, inp, n_tokens, seed):
+    """The oracle, as it stands, on the host cores: routing of every token and
+    the expert outputs of n_tokens sampled tokens."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from synthetic import to_numpy
+
+    mode = oracle.SIGMOID if w.score_fn == "sigmoid" else oracle.SOFTMAX
+    u = to_numpy(inp["u"])
+    Wr = to_numpy(inp["W_router"])
+    bias = inp["bias"].double().cpu().numpy()
+    threads = oracle.default_threads()
+    t = time.perf_counter()
+    idx, _, _, _, _ = oracle.route(u, Wr, w.k, mode, w.n_groups, w.topk_groups, w.route_scale,
+                                   bias=bias, nthreads=threads)
+    t_route = time.perf_counter() - t
+    rng = np.random.default_rng(seed)
+    tok = np.sort(rng.choice(w.T, size=min(n_tokens, w.T), replace=False))
+    sel = idx[tok].astype(np.int64)
+    used = np.unique(sel)
+    remap = np.full(w.E, -1, dtype=np.int64)
+    remap[used] = np.arange(used.size)
+    t = time.perf_counter()
+    ui = torch.from_numpy(used).to(inp["W1"].device)
+    W1 = to_numpy(inp["W1"].index_select(0, ui))
+    W3 = to_numpy(inp["W3"].index_select(0, ui))
+    W2 = to_numpy(inp["W2"].index_select(0, ui))
+    shared = None if inp["shared"] is None else tuple(to_numpy(x) for x in inp["shared"])
+    t_copy = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.forward(u[tok], Wr[used], W1, W3, W2, w.k, shared=shared, score_fn=mode,
+                   route_scale=w.route_scale, forced_idx=remap[sel], nthreads=threads)
+    t_ffn = time.perf_counter() - t
+    n = tok.size
+    value = n / (t_ffn + t_route * n / w.T)
+    return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{w.name}: routing of all {w.T} tokens ({t_route:.2f} s) + expert and "
+                       f"shared outputs of {n} seeded random tokens ({t_ffn:.2f} s); tokens/s = "
+                       f"n / (t_ffn + t_route * n / T); device-to-host copy of the "
+                       f"{used.size} experts used ({t_copy:.2f} s) excluded")}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); this layer build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_ffn_biased_amd as moe
+    from synthetic import WORKLOADS, make_inputs, make_u
+
+    moe.lib()
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    log(f"[bench] generating {w.name} inputs on {dev}")
+    inp = make_inputs(w, seed=args.seed, device=dev)
+    torch.cuda.synchronize()
+
+    log(f"[bench] {w.name}: {args.warmup} warm-up + {args.steps} timed steps")
+    ms, wall, stage_ms, idx = run_layer(w, inp, inp["u"], args.steps, args.warmup, torch)
+    tokens_per_s = w.T / (ms * 1e-3)
+    layer_tflops = w.flops / (ms * 1e-3) / 1e12
+    S = w.T * w.k
+    gu_flops = 4.0 * w.d * (w.F * S + w.Fs * w.T)
+    gu_ms = stage_ms[GATE_UP]
+    gu_tflops = gu_flops / (gu_ms * 1e-3) / 1e12
+    traffic = stored_traffic(f"gate_up_{w.name}")
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; u ~ N(0,1), weights ~ N(0, 1/fan_in), bias ~ U(-0.05, 0.05))",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F,
+                   "F_shared": w.Fs, "score_fn": w.score_fn, "n_groups": w.n_groups,
+                   "topk_groups": w.topk_groups, "route_scale": w.route_scale},
+        "layer_tflops": round(layer_tflops, 2),
+        "layer_mfma_frac": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
+        "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, stage_ms)},
+        "roofline": {"kernel": "grouped_gemm_bf16<gate_up>", "bound": "mfma",
+                     "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+
+    if not args.no_decode:
+        wd = WORKLOADS[args.decode_workload]
+        ud = make_u(wd, seed=args.seed, device=dev)
+        log(f"[bench] {wd.name}: {args.warmup} warm-up + {args.decode_steps} timed steps")
+        dms, _, dstage, didx = run_layer(wd, inp, ud, args.decode_steps, args.warmup, torch)
+        hit = int(torch.unique(didx).numel())
+        s = 2
+        gu_bytes = (hit * 2 * wd.F * wd.d + 2 * wd.Fs * wd.d) * s + wd.T * wd.d * s + \
+            (wd.T * wd.k * wd.F + wd.T * wd.Fs) * s
+        layer_bytes = (wd.E * wd.d * s + 4 * wd.E + hit * 3 * wd.d * wd.F * s + 3 * wd.d * wd.Fs * s
+                       + 2 * wd.T * wd.d * s + 8 * wd.T * wd.k)
+        gbs = layer_bytes / (dms * 1e-3) / 1e9
+        gu_gbs = gu_bytes / (dstage[GATE_UP] * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": wd.name, "T": wd.T, "ms_per_step": round(dms, 4),
+            "tokens_per_s": round(wd.T / (dms * 1e-3), 1), "experts_hit": hit,
+            "layer_bytes": layer_bytes, "layer_GBps": round(gbs, 1),
+            "layer_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, dstage)},
+            "roofline": {"kernel": "grouped_gemm_bf16<gate_up>", "bound": "hbm",
+                         "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
+                         "traffic": stored_traffic(f"gate_up_{wd.name}")},
+        }
+
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens, args.seed)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -105,6 +105,22 @@ def torch_dtype(w: Workload):
     return torch.float32 if w.dtype == "f32" else torch.bfloat16
 
 
+def _make_u(w: Workload, seed, dev):
+    u = _randn((w.T, w.d), _gen(seed, "u", dev), dev, 1.0, torch.float32)
+    m = None
+    if w.skew:
+        m = torch.randn(w.d, generator=_gen(seed, "skew_dir", dev), device=dev,
+                        dtype=torch.float32)
+        m = m / m.norm()
+        u = u + w.skew_shift * m
+    return u.to(torch_dtype(w)), m
+
+
+def make_u(w: Workload, seed: int = 0, device="cpu") -> torch.Tensor:
+    """The token inputs of ``w`` alone (same draw as in make_inputs)."""
+    return _make_u(w, seed, torch.device(device))[0]
+
+
 def make_inputs(w: Workload, seed: int = 0, device="cpu", bias: Optional[torch.Tensor] = None,
                 expert0_scale: Optional[float] = None) -> dict:
     """All inputs of one layer call as torch tensors on ``device``.
@@ -114,13 +130,7 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", bias: Optional[torch.T
     dt = torch_dtype(w)
     dev = torch.device(device)
     T, d, E, F, Fs = w.T, w.d, w.E, w.F, w.Fs
-    u = _randn((T, d), _gen(seed, "u", dev), dev, 1.0, torch.float32)
-    m = None
-    if w.skew:
-        m = torch.randn(d, generator=_gen(seed, "skew_dir", dev), device=dev, dtype=torch.float32)
-        m = m / m.norm()
-        u = u + w.skew_shift * m
-    u = u.to(dt)
+    u, m = _make_u(w, seed, dev)
     Wr = _randn((E, d), _gen(seed, "W_router", dev), dev, 1.0 / math.sqrt(d), torch.float32)
     if w.skew and expert0_scale is not None:
         Wr[0] = float(expert0_scale) * m
