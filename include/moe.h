@@ -133,6 +133,15 @@ moe_status moe_route_debug(const void *u, const void *W_router, const float *bia
                            int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Which grouped-GEMM kernels moe_layer_forward uses for cfg (host only, no
+ * GPU call): *gemm_path = 0 for the tiled kernels (any size, fp32 or bf16),
+ * 1 for the persistent weight-streaming kernels (bf16, d % 256 == 0,
+ * F % 128 == 0, F_shared % 128 == 0, at least 64 routed rows per expert on
+ * average); *tile_rows = rows per GEMM tile.  Either pointer may be NULL.
+ */
+moe_status moe_plan_describe(const moe_cfg *cfg, int32_t *gemm_path, int32_t *tile_rows);
+
 /* Human-readable text of a status code (static storage). */
 const char *moe_status_str(int status);
 

@@ -101,6 +101,9 @@ def lib():
         L.moe_layer_forward.restype = I32
         L.moe_route_debug.argtypes = [P, P, P, CP, P, P, P, P, P, P, P, SZ, P]
         L.moe_route_debug.restype = I32
+        L.moe_plan_describe.argtypes = [CP, ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.POINTER(ctypes.c_int32)]
+        L.moe_plan_describe.restype = I32
         L.moe_status_str.argtypes = [I32]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_timing_enable.argtypes = [I32]
@@ -118,6 +121,19 @@ def moe_status_str(status: int) -> str:
 def moe_check_cfg(cfg: MoeConfig) -> int:
     c = cfg.to_c()
     return int(lib().moe_check_cfg(ctypes.byref(c)))
+
+
+GEMM_PATHS = {0: "tiled", 1: "stream"}
+
+
+def moe_plan_describe(cfg: MoeConfig):
+    """(gemm path name, rows per GEMM tile) the library uses for cfg."""
+    c = cfg.to_c()
+    path, rows = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    st = lib().moe_plan_describe(ctypes.byref(c), ctypes.byref(path), ctypes.byref(rows))
+    if st != 0:
+        raise MoeError(st, "moe_plan_describe")
+    return GEMM_PATHS[path.value], rows.value
 
 
 def moe_workspace_bytes(cfg: MoeConfig) -> int:

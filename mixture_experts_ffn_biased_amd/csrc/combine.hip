@@ -1,4 +1,5 @@
 // Stage 5: gate-weighted combine, y[t] = Z[t] + sum_j gates[t][j] * O[inv[t*k+j]].
+// Z and O are in the layer dtype; the sum is accumulated in fp32.
 //
 // "Sparse MoE FFN" (DeepSeek-V3), eq. 12 and "Packed forward": the routed
 // outputs are scaled by their gates and summed, the shared output is added
@@ -13,7 +14,7 @@ namespace moe {
 namespace {
 
 __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__ O,
-                                                    const float *__restrict__ Z,
+                                                    const uint16_t *__restrict__ Z,
                                                     const int32_t *__restrict__ inv,
                                                     const float *__restrict__ gates, int64_t T,
                                                     int d, int k, uint16_t *__restrict__ y) {
@@ -29,10 +30,13 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
   for (int c = threadIdx.x; c < nchunk; c += 256) {
     float acc[8];
     if (Z) {
-      const float4 z0 = *reinterpret_cast<const float4 *>(Z + t * d + c * 8);
-      const float4 z1 = *reinterpret_cast<const float4 *>(Z + t * d + c * 8 + 4);
-      acc[0] = z0.x; acc[1] = z0.y; acc[2] = z0.z; acc[3] = z0.w;
-      acc[4] = z1.x; acc[5] = z1.y; acc[6] = z1.z; acc[7] = z1.w;
+      const uint4 z = *reinterpret_cast<const uint4 *>(Z + t * d + c * 8);
+      const uint32_t zw[4] = {z.x, z.y, z.z, z.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = bf16_to_f32(static_cast<uint16_t>(zw[i] & 0xffffu));
+        acc[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(zw[i] >> 16));
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -87,14 +91,16 @@ __global__ __launch_bounds__(256) void combine_f32(const float *__restrict__ O,
 
 hipError_t launch_combine(const Plan &p, const float *gates, void *y, hipStream_t s) {
   const moe_cfg &c = p.cfg;
-  const float *Z = c.F_shared > 0 ? p.Z : nullptr;
+  const void *Z = c.F_shared > 0 ? p.Z : nullptr;
   const dim3 grid(static_cast<unsigned>(c.T));
   if (c.dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bf16, grid, dim3(256), 0, s, static_cast<const uint16_t *>(p.O), Z,
-                       p.inv, gates, c.T, c.d, c.k, static_cast<uint16_t *>(y));
+    hipLaunchKernelGGL(combine_bf16, grid, dim3(256), 0, s, static_cast<const uint16_t *>(p.O),
+                       static_cast<const uint16_t *>(Z), p.inv, gates, c.T, c.d, c.k,
+                       static_cast<uint16_t *>(y));
   else
-    hipLaunchKernelGGL(combine_f32, grid, dim3(256), 0, s, static_cast<const float *>(p.O), Z, p.inv,
-                       gates, c.T, c.d, c.k, static_cast<float *>(y));
+    hipLaunchKernelGGL(combine_f32, grid, dim3(256), 0, s, static_cast<const float *>(p.O),
+                       static_cast<const float *>(Z), p.inv, gates, c.T, c.d, c.k,
+                       static_cast<float *>(y));
   return hipGetLastError();
 }
 

@@ -1,0 +1,469 @@
+// Grouped expert GEMMs for prefill-sized groups (many rows per expert): a
+// persistent, XCD-aware, weight-streaming kernel for gfx950.
+//
+// Same two products as grouped_gemm.hip (the SwiGLU expert of "Sparse MoE
+// FFN" (DeepSeek-V3), "How it works", batched as grouped GEMMs as "Mixture of
+// experts and architecture families", "The router and load balancing",
+// suggests); only the schedule and the data movement differ:
+//
+//  * One 256-thread workgroup per CU loops over work items (tile, n-slab).
+//    Items are kept in eight per-XCD lists: a chunk (up to two 256-row tiles
+//    of one expert) goes to one XCD with all its n-slabs, the tiles of a
+//    chunk adjacent.  Workgroups of an XCD take items from their list in
+//    order through an atomic counter, so the workgroups running together on
+//    an XCD share the expert's token rows and weight slabs in that XCD's L2,
+//    and each weight byte is fetched from HBM about once.  A workgroup whose
+//    list is empty takes items from the other XCDs' lists.
+//  * Tiles of 256 rows x 256 weight rows x 32, staged by direct global-to-LDS
+//    16-byte loads (global_load_lds_dwordx4) through a 4-stage ring, so three
+//    stages (96 KB) are in flight while one is multiplied; no VGPR staging.
+//  * Four waves in a 2x2 grid, each 128 x 128 of v_mfma_f32_32x32x16_bf16
+//    with fp32 accumulators.  Rows past an expert's count are not multiplied.
+//  * gate_up: the 256 weight rows of a slab are 64 rows of W1 then 64 of W3
+//    per wave column, so SiLU(x W1^T) * (x W3^T) meets in the same lane;
+//    the bf16 result goes through LDS to 16-byte stores.
+#include "common.hpp"
+#include "plan.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int SBM = 256, SBN = 256, SBK = 32, NSTAGE = 4;
+constexpr int A_BYTES = SBM * SBK * 2;
+constexpr int B_BYTES = SBN * SBK * 2;
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that neither waits for the in-flight LDS loads nor lets
+// the compiler move memory accesses across it.
+__device__ __forceinline__ void raw_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+struct StreamArgs {
+  const Tile *tiles;
+  const int2 *items;        // per-XCD segments of {tile id, n-slab}
+  const int32_t *xcd_off;   // [8] segment starts
+  const int32_t *xcd_cnt;   // [8] segment lengths
+  int32_t *counters;        // [8] zero on entry
+  const int32_t *perm;      // gate_up: position -> slot
+  int k;
+  int E;
+  const void *A_routed, *A_shared;
+  int gather;
+  const void *B0_routed, *B1_routed, *B0_shared, *B1_shared;
+  int N_routed, N_shared, K_routed, K_shared;
+  void *C_routed, *C_shared;
+};
+
+template <bool DUAL>
+__device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, unsigned char *r0,
+                                         unsigned char *r1, unsigned char *r2, unsigned char *r3) {
+  unsigned char *const ring[NSTAGE] = {r0, r1, r2, r3};
+  const Tile tl = g.tiles[item.x];
+  const bool shared = tl.group == g.E;
+  const int N = shared ? g.N_shared : g.N_routed;
+  const int K = shared ? g.K_shared : g.K_routed;
+  const int n0 = item.y * (DUAL ? SBN / 2 : SBN);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const uint16_t *A = static_cast<const uint16_t *>(shared ? g.A_shared : g.A_routed);
+  const uint16_t *B0 = static_cast<const uint16_t *>(shared ? g.B0_shared : g.B0_routed);
+  const uint16_t *B1 = static_cast<const uint16_t *>(shared ? g.B1_shared : g.B1_routed);
+  if (!shared) {
+    const int64_t es = static_cast<int64_t>(N) * K;
+    B0 += tl.group * es;
+    if (DUAL) B1 += tl.group * es;
+  }
+
+  // DMA sources: instruction i of this wave fills LDS rows (wave*4+i)*16 ..
+  // +16 of the A and B tiles; lane l lands in row +l/4, physical chunk l%4,
+  // which holds logical k-chunk (l%4) ^ ((row>>2)&3).
+  const uint16_t *ap[4];
+  const uint16_t *bp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 4 + i) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int rr = r < tl.nrows ? r : 0;
+    int64_t arow;
+    if (g.gather && !shared)
+      arow = g.perm[tl.row0 + rr] / g.k;
+    else
+      arow = static_cast<int64_t>(tl.row0) + rr;
+    ap[i] = A + arow * K + c * 8;
+    int64_t brow;
+    const uint16_t *bsrc = B0;
+    if (DUAL) {
+      const int q = r & 127;
+      brow = n0 + (r >> 7) * 64 + (q & 63);
+      if (q >= 64) bsrc = B1;
+    } else {
+      brow = n0 + r;
+    }
+    bp[i] = bsrc + brow * K + c * 8;
+  }
+
+  auto issue = [&](unsigned char *st, int kt) {
+    const int koff = kt * SBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(ap[i] + koff, (lds_void *)(st + (wave * 4 + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(bp[i] + koff, (lds_void *)(st + A_BYTES + (wave * 4 + i) * 1024),
+                                       16, 0, 0);
+  };
+
+  // Fragment offsets: row = base + (lane & 31), logical chunk kk*2 + lane/32,
+  // swizzle term depends on lane bits 2..3 only.
+  const int sw = (lane >> 2) & 3;
+  const int fo0 = (lane & 31) * 64 + (((0 + (lane >> 5)) ^ sw) << 4);
+  const int fo1 = (lane & 31) * 64 + (((2 + (lane >> 5)) ^ sw) << 4);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  // Rows of this wave's half (<= 0: the wave's results are discarded).
+  const int rows_here = tl.nrows - wm * 128;
+  const int KT = K / SBK;
+
+  auto compute = [&](const unsigned char *st) {
+    const unsigned char *sa = st + wm * 128 * 64;
+    const unsigned char *sb = st + A_BYTES + wn * 128 * 64;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int fo = kk ? fo1 : fo0;
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) a[mi] = *reinterpret_cast<const bf16x8 *>(sa + mi * 32 * 64 + fo);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) b[ni] = *reinterpret_cast<const bf16x8 *>(sb + ni * 32 * 64 + fo);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+  };
+
+  // The previous item's stores and loads are complete before the ring refills.
+  wait_vmcnt<0>();
+  raw_barrier();
+  issue(ring[0], 0);
+  issue(ring[1], 1);
+  issue(ring[2], 2);
+  // Stage kt lives in ring slot kt % 4 (unrolled by 4 so every slot index is
+  // static).  Stage kt is complete once at most the two later stages (8
+  // loads each) are outstanding; after the barrier stage kt+3 refills the
+  // slot stage kt-1 used.
+  const int KG = KT / NSTAGE;  // K is a multiple of 4 stages
+  for (int j = 0; j < KG - 1; ++j) {
+    const int kt = j * NSTAGE;
+#pragma unroll
+    for (int s4 = 0; s4 < NSTAGE; ++s4) {
+      wait_vmcnt<16>();
+      raw_barrier();
+      issue(ring[(s4 + 3) & 3], kt + s4 + 3);
+      compute(ring[s4]);
+    }
+  }
+  wait_vmcnt<16>();
+  raw_barrier();
+  issue(ring[3], KT - 1);
+  compute(ring[0]);
+  wait_vmcnt<16>();
+  raw_barrier();
+  compute(ring[1]);
+  wait_vmcnt<8>();
+  raw_barrier();
+  compute(ring[2]);
+  wait_vmcnt<0>();
+  raw_barrier();
+  compute(ring[3]);
+  // Every wave is done reading the ring before it is reused for the output.
+  raw_barrier();
+
+  const int row_lane = 4 * (lane >> 5);
+  if (DUAL) {
+    // H tile: 256 rows x 128 columns bf16 (256 bytes a row); rows 0..127 in
+    // ring slot 0, rows 128..255 in slot 1.
+    if (rows_here > 0) {
+      uint16_t *Ht = reinterpret_cast<uint16_t *>(wm ? ring[1] : ring[0]);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = mi * 32 + 8 * (r >> 2) + row_lane + (r & 3);
+            const int col = wn * 64 + ni * 32 + (lane & 31);
+            Ht[row * 128 + col] = f32_to_bf16(silu(acc[mi][ni][r]) * acc[mi][ni + 2][r]);
+          }
+    }
+    __syncthreads();
+    uint16_t *C = static_cast<uint16_t *>(shared ? g.C_shared : g.C_routed);
+#pragma unroll 4
+    for (int j = 0; j < 16; ++j) {
+      const int q = tid + 256 * j;
+      const int row = q >> 4, ch = q & 15;
+      const uint16_t *Ht = reinterpret_cast<const uint16_t *>(row < 128 ? ring[0] : ring[1]);
+      if (row < tl.nrows)
+        *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
+            *reinterpret_cast<const uint4 *>(Ht + (row & 127) * 128 + ch * 8);
+    }
+    __syncthreads();
+  } else {
+    // Output tile: 256 x 256 bf16 (512 bytes a row); rows 64*s .. 64*s+63 in
+    // ring slot s.
+    if (rows_here > 0) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        uint16_t *Ot = reinterpret_cast<uint16_t *>(ring[wm * 2 + (mi >> 1)]);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = (mi & 1) * 32 + 8 * (r >> 2) + row_lane + (r & 3);
+            const int col = wn * 128 + ni * 32 + (lane & 31);
+            Ot[row * 256 + col] = f32_to_bf16(acc[mi][ni][r]);
+          }
+      }
+    }
+    __syncthreads();
+    uint16_t *C = static_cast<uint16_t *>(shared ? g.C_shared : g.C_routed);
+#pragma unroll 4
+    for (int j = 0; j < 32; ++j) {
+      const int q = tid + 256 * j;
+      const int row = q >> 5, ch = q & 31;
+      const unsigned char *slot = row < 128 ? (row < 64 ? ring[0] : ring[1]) : (row < 192 ? ring[2] : ring[3]);
+      if (row < tl.nrows)
+        *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
+            *reinterpret_cast<const uint4 *>(slot + (row & 63) * 512 + ch * 16);
+    }
+    __syncthreads();
+  }
+}
+
+template <bool DUAL>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_stream(StreamArgs g) {
+  // Four separate ring slots: the compiler can then tell the LDS loads into
+  // one slot from the reads of another and adds no waits of its own.
+  __shared__ __attribute__((aligned(16))) unsigned char ring0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char ring2[STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char ring3[STAGE_BYTES];
+  __shared__ int item_sh;
+  const int xcd = blockIdx.x & 7;
+  for (int o = 0; o < 8; ++o) {
+    const int x = (xcd + o) & 7;
+    const int cnt = g.xcd_cnt[x];
+    const int off = g.xcd_off[x];
+    for (;;) {
+      if (threadIdx.x == 0) item_sh = atomicAdd(&g.counters[x], 1);
+      __syncthreads();
+      const int it = item_sh;
+      __syncthreads();
+      if (it >= cnt) break;
+      run_item<DUAL>(g, g.items[off + it], ring0, ring1, ring2, ring3);
+    }
+  }
+}
+
+// ---- schedule: per-XCD item lists ------------------------------------------
+
+constexpr int kMaxChunks = 4096;
+
+// One block.  Rebuilds the tile numbering of perm_scan (experts in order,
+// ceil(count/256) tiles each, then the shared expert's tiles), groups tiles
+// into chunks of up to two per expert, deals chunks to XCDs round-robin and
+// writes both GEMMs' item lists (tile fastest, then n-slab, within a chunk).
+__global__ __launch_bounds__(256) void stream_schedule(
+    const int32_t *__restrict__ counts, int E, int64_t T, int has_shared, int nt_gu_r, int nt_gu_s,
+    int nt_dn_r, int nt_dn_s, int2 *__restrict__ items_gu, int2 *__restrict__ items_dn,
+    int32_t *__restrict__ meta /* [2][3][8]: off, cnt, counter for gate_up, down */) {
+  __shared__ int cfirst[kMaxChunks];
+  __shared__ unsigned char cmt[kMaxChunks];
+  __shared__ int cpos[2][kMaxChunks];
+  __shared__ int buf[256];
+  __shared__ int xtot[2][8];
+  __shared__ int xoff[2][8];
+  const int tid = threadIdx.x;
+  const int e = tid;
+  const int c = e < E ? counts[e] : 0;
+  const int nt = (c + SBM - 1) / SBM;
+  const int nch = (nt + 1) / 2;
+  // exclusive scans of tiles and chunks
+  buf[tid] = nt;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = tid >= o ? buf[tid - o] : 0;
+    __syncthreads();
+    buf[tid] += v;
+    __syncthreads();
+  }
+  const int tile_off = buf[tid] - nt;
+  const int routed_tiles = buf[255];
+  __syncthreads();
+  buf[tid] = nch;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = tid >= o ? buf[tid - o] : 0;
+    __syncthreads();
+    buf[tid] += v;
+    __syncthreads();
+  }
+  const int chunk_off = buf[tid] - nch;
+  const int routed_chunks = buf[255];
+  __syncthreads();
+  for (int j = 0; j < nch; ++j) {
+    cfirst[chunk_off + j] = tile_off + 2 * j;
+    cmt[chunk_off + j] = static_cast<unsigned char>(nt - 2 * j < 2 ? nt - 2 * j : 2);
+  }
+  int n_chunks = routed_chunks;
+  if (has_shared) {
+    const int ns = static_cast<int>((T + SBM - 1) / SBM);
+    const int nsc = (ns + 1) / 2;
+    for (int j = tid; j < nsc; j += 256) {
+      cfirst[routed_chunks + j] = routed_tiles + 2 * j;
+      cmt[routed_chunks + j] = static_cast<unsigned char>(ns - 2 * j < 2 ? ns - 2 * j : 2);
+    }
+    n_chunks += nsc;
+  }
+  __syncthreads();
+  if (tid < 16) {
+    const int x = tid & 7, list = tid >> 3;
+    int pos = 0;
+    for (int ch = x; ch < n_chunks; ch += 8) {
+      cpos[list][ch] = pos;
+      const bool sh = ch >= routed_chunks;
+      const int ntl = list == 0 ? (sh ? nt_gu_s : nt_gu_r) : (sh ? nt_dn_s : nt_dn_r);
+      pos += cmt[ch] * ntl;
+    }
+    xtot[list][x] = pos;
+  }
+  __syncthreads();
+  if (tid < 2) {
+    int run = 0;
+    for (int x = 0; x < 8; ++x) {
+      xoff[tid][x] = run;
+      meta[tid * 24 + x] = run;
+      meta[tid * 24 + 8 + x] = xtot[tid][x];
+      meta[tid * 24 + 16 + x] = 0;
+      run += xtot[tid][x];
+    }
+  }
+  __syncthreads();
+  for (int ch = tid; ch < n_chunks; ch += 256) {
+    const bool sh = ch >= routed_chunks;
+    const int mt = cmt[ch];
+    for (int list = 0; list < 2; ++list) {
+      const int ntl = list == 0 ? (sh ? nt_gu_s : nt_gu_r) : (sh ? nt_dn_s : nt_dn_r);
+      int2 *out = (list == 0 ? items_gu : items_dn) + xoff[list][ch & 7] + cpos[list][ch];
+      for (int n = 0; n < ntl; ++n)
+        for (int m = 0; m < mt; ++m) out[n * mt + m] = make_int2(cfirst[ch] + m, n);
+    }
+  }
+}
+
+int g_num_cus = 0;
+
+int num_cus() {
+  if (g_num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      g_num_cus = n;
+    else
+      g_num_cus = 256;
+  }
+  return g_num_cus;
+}
+
+StreamArgs base_args(const Plan &p, int list) {
+  StreamArgs a{};
+  a.tiles = p.tiles;
+  a.items = list == 0 ? p.items_gu : p.items_dn;
+  a.xcd_off = p.sched_meta + list * 24;
+  a.xcd_cnt = p.sched_meta + list * 24 + 8;
+  a.counters = p.sched_meta + list * 24 + 16;
+  a.perm = p.perm;
+  a.k = p.cfg.k;
+  a.E = p.cfg.E;
+  return a;
+}
+
+}  // namespace
+
+int stream_tile_m() { return SBM; }
+int stream_max_chunks() { return kMaxChunks; }
+int stream_nslab_gate_up(int F) { return F / (SBN / 2); }
+int stream_nslab_down(int d) { return d / SBN; }
+
+hipError_t launch_stream_schedule(const Plan &p, hipStream_t s) {
+  const moe_cfg &c = p.cfg;
+  hipLaunchKernelGGL(stream_schedule, dim3(1), dim3(256), 0, s, p.counts, c.E, c.T, c.F_shared > 0 ? 1 : 0,
+                     c.F / (SBN / 2), c.F_shared / (SBN / 2), c.d / SBN, c.d / SBN, p.items_gu, p.items_dn,
+                     p.sched_meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_gate_up(const Plan &p, const void *u, const void *W1, const void *W3,
+                                 const void *W1s, const void *W3s, hipStream_t s) {
+  const moe_cfg &c = p.cfg;
+  StreamArgs a = base_args(p, 0);
+  a.A_routed = u;
+  a.A_shared = u;
+  a.gather = 1;
+  a.B0_routed = W1;
+  a.B1_routed = W3;
+  a.B0_shared = W1s;
+  a.B1_shared = W3s;
+  a.N_routed = c.F;
+  a.N_shared = c.F_shared;
+  a.K_routed = c.d;
+  a.K_shared = c.d;
+  a.C_routed = p.H;
+  a.C_shared = p.Hs;
+  hipLaunchKernelGGL(grouped_gemm_stream<true>, dim3(num_cus()), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_down(const Plan &p, const void *W2, const void *W2s, hipStream_t s) {
+  const moe_cfg &c = p.cfg;
+  StreamArgs a = base_args(p, 1);
+  a.A_routed = p.H;
+  a.A_shared = p.Hs;
+  a.gather = 0;
+  a.B0_routed = W2;
+  a.B1_routed = nullptr;
+  a.B0_shared = W2s;
+  a.B1_shared = nullptr;
+  a.N_routed = c.d;
+  a.N_shared = c.d;
+  a.K_routed = c.F;
+  a.K_shared = c.F_shared;
+  a.C_routed = p.O;
+  a.C_shared = p.Z;
+  hipLaunchKernelGGL(grouped_gemm_stream<false>, dim3(num_cus()), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

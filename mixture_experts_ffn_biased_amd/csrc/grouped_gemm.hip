@@ -8,7 +8,7 @@
 //
 //   gate_up: H[row] = SiLU(x W1^T) * (x W3^T), x = u[token of row]  (gather)
 //   down:    O[row] = H[row] W2^T   (routed rows, bf16 or fp32)
-//            Z[t]   = Hs[t] W2s^T   (shared rows, fp32)
+//            Z[t]   = Hs[t] W2s^T   (shared rows)
 //
 // Both are C = A B^T with A [rows][K] and B [N][K] row-major (K contiguous),
 // the layout in which the weights arrive.  bf16 runs on the gfx950 MFMA
@@ -341,7 +341,7 @@ hipError_t launch_down(const Plan &p, const void *W2, const void *W2s, hipStream
   g.K_shared = c.F_shared;
   g.C_routed = p.O;
   g.C_shared = p.Z;
-  g.c_shared_f32 = 1;
+  g.c_shared_f32 = 0;
   return launch_on(p, g, false, c.d, s);
 }
 

@@ -35,10 +35,25 @@ moe_status validate(const moe_cfg *c) {
 
 static size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// The streaming kernels need bf16, 256-row tiles with whole 128-column
+// gate/up slabs and 256-column down slabs, and enough rows per expert for a
+// 256-row tile to pay off; everything else takes the tiled kernels.
+static int choose_path(const moe_cfg &c) {
+  if (c.dtype != MOE_BF16) return PATH_TILED;
+  if (c.d % 256 != 0 || c.F % 128 != 0 || c.F_shared % 128 != 0) return PATH_TILED;
+  const int64_t S = c.T * c.k;
+  if (S < 64LL * c.E) return PATH_TILED;
+  const int64_t m = stream_tile_m();
+  const int64_t chunks = S / (2 * m) + c.E + c.T / (2 * m) + 4;
+  if (chunks > stream_max_chunks()) return PATH_TILED;
+  return PATH_STREAM;
+}
+
 void make_plan(const moe_cfg &c, void *base, Plan *p) {
   p->cfg = c;
   p->S = c.T * c.k;
-  p->tile_m = gemm_tile_m(c.dtype);
+  p->path = choose_path(c);
+  p->tile_m = p->path == PATH_STREAM ? stream_tile_m() : gemm_tile_m(c.dtype);
   p->n_perm_blocks = (p->S + kPermChunk - 1) / kPermChunk;
   p->max_tiles = (p->S + p->tile_m - 1) / p->tile_m + c.E +
                  (c.F_shared > 0 ? (c.T + p->tile_m - 1) / p->tile_m : 0);
@@ -58,10 +73,19 @@ void make_plan(const moe_cfg &c, void *base, Plan *p) {
   p->inv = static_cast<int32_t *>(take(sizeof(int32_t) * p->S));
   p->tiles = static_cast<Tile *>(take(sizeof(Tile) * p->max_tiles));
   p->tile_count = static_cast<int32_t *>(take(sizeof(int32_t)));
+  p->max_items_gu = p->max_items_dn = 0;
+  if (p->path == PATH_STREAM) {
+    const int64_t nslab = stream_nslab_gate_up(c.F > c.F_shared ? c.F : c.F_shared);
+    p->max_items_gu = p->max_tiles * nslab;
+    p->max_items_dn = p->max_tiles * stream_nslab_down(c.d);
+  }
+  p->items_gu = static_cast<int2 *>(take(sizeof(int2) * p->max_items_gu));
+  p->items_dn = static_cast<int2 *>(take(sizeof(int2) * p->max_items_dn));
+  p->sched_meta = static_cast<int32_t *>(take(sizeof(int32_t) * 48));
   p->H = take(es * p->S * c.F);
   p->Hs = take(es * c.T * c.F_shared);
   p->O = take(es * p->S * c.d);
-  p->Z = static_cast<float *>(take(c.F_shared > 0 ? sizeof(float) * c.T * c.d : 0));
+  p->Z = take(c.F_shared > 0 ? es * c.T * c.d : 0);
   p->bytes = off;
 }
 
@@ -93,6 +117,16 @@ size_t moe_workspace_bytes(const moe_cfg *cfg) {
 }
 
 moe_status moe_check_cfg(const moe_cfg *cfg) { return validate(cfg); }
+
+moe_status moe_plan_describe(const moe_cfg *cfg, int32_t *gemm_path, int32_t *tile_rows) {
+  const moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  Plan p;
+  make_plan(*cfg, nullptr, &p);
+  if (gemm_path) *gemm_path = p.path;
+  if (tile_rows) *tile_rows = p.tile_m;
+  return MOE_OK;
+}
 
 const char *moe_status_str(int status) {
   switch (status) {
@@ -164,11 +198,14 @@ moe_status moe_layer_forward(const void *u, const void *W_router, const float *b
   mark(1);
   if (launch_permute(p, topk_idx, s) != hipSuccess) return MOE_ERR_HIP;
   mark(2);
-  if (launch_gate_up(p, u, W1, W3, shared ? shared->W1 : nullptr, shared ? shared->W3 : nullptr, s) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
+  const void *W1s = shared ? shared->W1 : nullptr, *W3s = shared ? shared->W3 : nullptr;
+  const void *W2s = shared ? shared->W2 : nullptr;
+  hipError_t err = p.path == PATH_STREAM ? launch_stream_gate_up(p, u, W1, W3, W1s, W3s, s)
+                                         : launch_gate_up(p, u, W1, W3, W1s, W3s, s);
+  if (err != hipSuccess) return MOE_ERR_HIP;
   mark(3);
-  if (launch_down(p, W2, shared ? shared->W2 : nullptr, s) != hipSuccess) return MOE_ERR_HIP;
+  err = p.path == PATH_STREAM ? launch_stream_down(p, W2, W2s, s) : launch_down(p, W2, W2s, s);
+  if (err != hipSuccess) return MOE_ERR_HIP;
   mark(4);
   if (launch_combine(p, gates, y, s) != hipSuccess) return MOE_ERR_HIP;
   mark(5);

@@ -127,6 +127,10 @@ hipError_t launch_permute(const Plan &p, const int32_t *topk_idx, hipStream_t s)
                      p.tiles, p.tile_count);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (p.path == PATH_STREAM) {
+    err = launch_stream_schedule(p, s);
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(perm_scatter, dim3(nblk), dim3(256), 0, s, topk_idx, p.S, c.E, p.blk_base,
                      p.perm, p.inv);
   return hipGetLastError();

@@ -25,8 +25,15 @@ constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxGroups = 64;
 
+// Which grouped-GEMM kernels run the experts.
+enum GemmPath {
+  PATH_TILED = 0,   // grouped_gemm.hip: 128-row tiles (fp32 too), any size multiple of 64
+  PATH_STREAM = 1,  // gemm_stream.hip: persistent, 256-row tiles, bf16 prefill shapes
+};
+
 struct Plan {
   moe_cfg cfg;
+  int path;         // GemmPath
   int64_t S;        // routed slots, T*k
   int tile_m;       // rows per grouped-GEMM tile
   int64_t n_perm_blocks;
@@ -40,10 +47,14 @@ struct Plan {
   int32_t *inv;         // [S]  position of each slot
   Tile *tiles;          // [max_tiles]
   int32_t *tile_count;  // [1]
+  int2 *items_gu;       // PATH_STREAM: per-XCD work lists of the gate/up GEMM
+  int2 *items_dn;       //              and of the down GEMM
+  int32_t *sched_meta;  //              [2][3][8] list offsets, lengths, counters
+  int64_t max_items_gu, max_items_dn;
   void *H;              // [S][F]        SiLU(W1 x) * W3 x of each routed slot
   void *Hs;             // [T][F_shared] same for the shared expert
   void *O;              // [S][d]        expert output of each routed slot
-  float *Z;             // [T][d]        shared expert output (fp32)
+  void *Z;              // [T][d]        shared expert output (layer dtype)
   size_t bytes;
 };
 
@@ -58,5 +69,14 @@ hipError_t launch_gate_up(const Plan &p, const void *u, const void *W1, const vo
                           const void *W1s, const void *W3s, hipStream_t s);
 hipError_t launch_down(const Plan &p, const void *W2, const void *W2s, hipStream_t s);
 hipError_t launch_combine(const Plan &p, const float *gates, void *y, hipStream_t s);
+
+int stream_tile_m();
+int stream_max_chunks();
+int stream_nslab_gate_up(int F);
+int stream_nslab_down(int d);
+hipError_t launch_stream_schedule(const Plan &p, hipStream_t s);
+hipError_t launch_stream_gate_up(const Plan &p, const void *u, const void *W1, const void *W3,
+                                 const void *W1s, const void *W3s, hipStream_t s);
+hipError_t launch_stream_down(const Plan &p, const void *W2, const void *W2s, hipStream_t s);
 
 }  // namespace moe

@@ -84,6 +84,16 @@ def test_workspace_grows_with_tokens_and_shared_expert():
         assert moe.moe_workspace_bytes(moe.MoeConfig.from_workload(w)) > 0
 
 
+def test_gemm_path_selection():
+    from synthetic import WORKLOADS
+    path = {n: moe.moe_plan_describe(moe.MoeConfig.from_workload(w))[0] for n, w in WORKLOADS.items()}
+    assert path["tiny_fp32"] == "tiled"
+    assert path["dsv3_prefill"] == "stream" and path["mixtral_e8_top2"] == "stream"
+    assert path["skewed_e128_top8"] == "stream"
+    assert moe.moe_plan_describe(cfg(d=192))[0] == "tiled"
+    assert moe.moe_plan_describe(cfg(T=8, n_groups=1, topk_groups=1))[0] == "tiled"
+
+
 def _call(c, **ptrs):
     """moe_layer_forward with fake (never dereferenced) aligned pointers."""
     L = moe.lib()

@@ -102,6 +102,39 @@ SMALL = {
 }
 
 
+STREAM = {
+    "stream_softmax": Workload("stream_softmax", 700, 256, 8, 2, 256, 0, "softmax", 1, 1, 1.0,
+                               "bf16", "zero"),
+    "stream_sigmoid_groups_shared": Workload("stream_sigmoid_groups_shared", 1200, 512, 16, 4, 384,
+                                             256, "sigmoid", 4, 2, 2.5, "bf16", "uniform"),
+    "stream_many_tiles": Workload("stream_many_tiles", 2100, 256, 8, 3, 128, 128, "softmax", 1, 1,
+                                  1.0, "bf16", "uniform"),
+}
+
+
+@pytest.mark.parametrize("name", list(STREAM))
+def test_stream_path_every_token(dev, name):
+    w = STREAM[name]
+    assert moe.moe_plan_describe(moe.MoeConfig.from_workload(w))[0] == "stream"
+    log(f"[stream] {name}")
+    inp = to_dev(make_inputs(w, seed=7, device="cpu"), dev)
+    y, idx, g = run(w, inp)
+    st = check_full(w, inp, y, idx, g)
+    log(f"[stream] {name} {st}")
+
+
+def test_stream_path_one_expert_takes_every_token(dev):
+    """Expert 0 in every token's set: 2100 rows = 9 tiles of 256 (ragged)
+    spread over several chunks and XCD lists."""
+    w = STREAM["stream_many_tiles"]
+    b = torch.zeros(w.E)
+    b[0] = 100.0
+    inp = to_dev(make_inputs(w, seed=8, device="cpu", bias=b), dev)
+    y, idx, g = run(w, inp)
+    assert (idx[:, 0] == 0).all()
+    check_full(w, inp, y, idx, g)
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_layer_every_token(dev, name):
     w = SMALL[name]
