@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="tokens whose expert outputs the CPU oracle computes")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB three times (a plain "
+                         "copy kernel of known size, to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -230,6 +233,15 @@ def main():
                          "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
                          "traffic": stored_traffic(f"gate_up_{wd.name}")},
         }
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")

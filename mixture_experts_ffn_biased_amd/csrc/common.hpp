@@ -55,21 +55,37 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float(b);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
-  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
-  lo = __shfl_xor(lo, mask, 64);
-  hi = __shfl_xor(hi, mask, 64);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+// One DPP step of a wave-wide unsigned 64-bit maximum: every lane takes the
+// larger of its value and the value of the lane dpp_ctrl names.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const int lo = static_cast<int>(static_cast<uint32_t>(v));
+  const int hi = static_cast<int>(static_cast<uint32_t>(v >> 32));
+  const uint32_t olo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false));
+  const uint32_t ohi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false));
+  const uint64_t o = (static_cast<uint64_t>(ohi) << 32) | olo;
+  return o > v ? o : v;
 }
 
-// Butterfly maximum over the 64 lanes of a wave; every lane gets the result.
+// Maximum over the 64 lanes of a wave, returned wave-uniform.  Within each
+// row of 16 lanes: swap neighbours, swap pairs (quad_perm), mirror halves
+// of 8, mirror the row (DPP); then the four row maxima by readlane.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_u64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_u64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_u64<0x141>(v);  // row_half_mirror
+  v = dpp_max_u64<0x140>(v);  // row_mirror
+  uint64_t best = 0;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint64_t o = shfl_xor_u64(v, m);
-    v = o > v ? o : v;
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 16 * r));
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 16 * r));
+    const uint64_t x = (static_cast<uint64_t>(hi) << 32) | lo;
+    best = x > best ? x : best;
   }
-  return v;
+  return best;
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {

@@ -6,7 +6,7 @@
 // experts and architecture families", "The router and load balancing",
 // suggests); only the schedule and the data movement differ:
 //
-//  * One 256-thread workgroup per CU loops over work items (tile, n-slab).
+//  * One 512-thread workgroup per CU loops over work items (tile, n-slab).
 //    Items are kept in eight per-XCD lists: a chunk (up to two 256-row tiles
 //    of one expert) goes to one XCD with all its n-slabs, the tiles of a
 //    chunk adjacent.  Workgroups of an XCD take items from their list in
@@ -17,39 +17,26 @@
 //  * Tiles of 256 rows x 256 weight rows x 32, staged by direct global-to-LDS
 //    16-byte loads (global_load_lds_dwordx4) through a 4-stage ring, so three
 //    stages (96 KB) are in flight while one is multiplied; no VGPR staging.
-//  * Four waves in a 2x2 grid, each 128 x 128 of v_mfma_f32_32x32x16_bf16
-//    with fp32 accumulators.  Rows past an expert's count are not multiplied.
-//  * gate_up: the 256 weight rows of a slab are 64 rows of W1 then 64 of W3
-//    per wave column, so SiLU(x W1^T) * (x W3^T) meets in the same lane;
-//    the bf16 result goes through LDS to 16-byte stores.
+//  * Eight waves in a 2x4 grid (two per SIMD, one from each row half), each
+//    128 x 64 of v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  A wave
+//    multiplies only the 32-row blocks that hold rows of the tile (its K loop
+//    is specialised on that count), so a SIMD's MFMA work follows the tile's
+//    row count, and each SIMD has a second wave to cover waits.
+//  * gate_up: the 256 weight rows of a slab are 32 rows of W1 then the same
+//    32 of W3 per wave column, so SiLU(x W1^T) * (x W3^T) meets in the same
+//    lane; the bf16 result goes through LDS to 16-byte stores.
 #include "common.hpp"
+#include "pipeline.hpp"
 #include "plan.hpp"
 
 namespace moe {
 namespace {
 
 constexpr int SBM = 256, SBN = 256, SBK = 32, NSTAGE = 4;
+constexpr int NTHREADS = 512;  // 8 waves: 2 row halves x 4 column quarters
 constexpr int A_BYTES = SBM * SBK * 2;
 constexpr int B_BYTES = SBN * SBK * 2;
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Workgroup barrier that neither waits for the in-flight LDS loads nor lets
-// the compiler move memory accesses across it.
-__device__ __forceinline__ void raw_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 struct StreamArgs {
   const Tile *tiles;
@@ -67,17 +54,84 @@ struct StreamArgs {
   void *C_routed, *C_shared;
 };
 
+// Ring slots of one workgroup (separate __shared__ arrays).
+struct Ring {
+  unsigned char *s[NSTAGE];
+};
+
+// The K loop of one item for a wave with NMI active 32-row blocks (0..4).
+// Every wave runs the same loads and barriers whatever its NMI, so waves
+// with different row counts stay in step.
+template <bool DUAL, int NMI>
+__device__ __forceinline__ void kloop(const Ring &ring, const uint16_t *const (&ap)[2],
+                                      const uint16_t *const (&bp)[2], int KT, int wave, int wm,
+                                      int wn, int fo0, int fo1, f32x16 (&acc)[4][2]) {
+  auto issue = [&](unsigned char *st, int kt) {
+    const int koff = kt * SBK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(ap[i] + koff, st + (wave * 2 + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(bp[i] + koff, st + A_BYTES + (wave * 2 + i) * 1024);
+  };
+  auto compute = [&](const unsigned char *st) {
+    if (NMI == 0) return;
+    const unsigned char *sa = st + wm * 128 * 64;
+    const unsigned char *sb = st + A_BYTES + wn * 64 * 64;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int fo = kk ? fo1 : fo0;
+      bf16x8 a[NMI > 0 ? NMI : 1], b[2];
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) a[mi] = *reinterpret_cast<const bf16x8 *>(sa + mi * 2048 + fo);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) b[ni] = *reinterpret_cast<const bf16x8 *>(sb + ni * 2048 + fo);
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+  };
+  constexpr int PS = 2 * 2;  // loads per wave per stage
+  issue(ring.s[0], 0);
+  issue(ring.s[1], 1);
+  issue(ring.s[2], 2);
+  // Stage kt lives in slot kt % 4 (unrolled by 4: static slot indices).  It
+  // is complete once at most the two later stages are outstanding; after
+  // the barrier, stage kt+3 refills the slot of stage kt-1.
+  for (int j = 0; j < KT / NSTAGE - 1; ++j) {
+#pragma unroll
+    for (int s4 = 0; s4 < NSTAGE; ++s4) {
+      wait_vmcnt<2 * PS>();
+      raw_barrier();
+      issue(ring.s[(s4 + 3) & 3], j * NSTAGE + s4 + 3);
+      compute(ring.s[s4]);
+    }
+  }
+  wait_vmcnt<2 * PS>();
+  raw_barrier();
+  issue(ring.s[3], KT - 1);
+  compute(ring.s[0]);
+  wait_vmcnt<2 * PS>();
+  raw_barrier();
+  compute(ring.s[1]);
+  wait_vmcnt<PS>();
+  raw_barrier();
+  compute(ring.s[2]);
+  wait_vmcnt<0>();
+  raw_barrier();
+  compute(ring.s[3]);
+}
+
 template <bool DUAL>
-__device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, unsigned char *r0,
-                                         unsigned char *r1, unsigned char *r2, unsigned char *r3) {
-  unsigned char *const ring[NSTAGE] = {r0, r1, r2, r3};
+__device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const Ring &ring) {
   const Tile tl = g.tiles[item.x];
   const bool shared = tl.group == g.E;
   const int N = shared ? g.N_shared : g.N_routed;
   const int K = shared ? g.K_shared : g.K_routed;
   const int n0 = item.y * (DUAL ? SBN / 2 : SBN);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
   const uint16_t *A = static_cast<const uint16_t *>(shared ? g.A_shared : g.A_routed);
   const uint16_t *B0 = static_cast<const uint16_t *>(shared ? g.B0_shared : g.B0_routed);
@@ -88,14 +142,15 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, unsigne
     if (DUAL) B1 += tl.group * es;
   }
 
-  // DMA sources: instruction i of this wave fills LDS rows (wave*4+i)*16 ..
-  // +16 of the A and B tiles; lane l lands in row +l/4, physical chunk l%4,
-  // which holds logical k-chunk (l%4) ^ ((row>>2)&3).
-  const uint16_t *ap[4];
-  const uint16_t *bp[4];
+  // DMA sources: load i of wave w fills LDS rows g*16 .. g*16+15 (g = 2w+i)
+  // of the A and B tiles; lane l lands in row +l/4, physical chunk l%4,
+  // which holds logical k-chunk (l%4) ^ ((row>>2)&3).  Rows past the tile's
+  // count read its first row (never stored).
+  const uint16_t *ap[2];
+  const uint16_t *bp[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wave * 4 + i) * 16 + (lane >> 2);
+  for (int i = 0; i < 2; ++i) {
+    const int r = (wave * 2 + i) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ ((r >> 2) & 3);
     const int rr = r < tl.nrows ? r : 0;
     int64_t arow;
@@ -107,153 +162,98 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, unsigne
     int64_t brow;
     const uint16_t *bsrc = B0;
     if (DUAL) {
-      const int q = r & 127;
-      brow = n0 + (r >> 7) * 64 + (q & 63);
-      if (q >= 64) bsrc = B1;
+      // 64 rows per wave column: 32 of W1, then the same 32 of W3.
+      const int q = r & 63;
+      brow = n0 + (r >> 6) * 32 + (q & 31);
+      if (q >= 32) bsrc = B1;
     } else {
       brow = n0 + r;
     }
     bp[i] = bsrc + brow * K + c * 8;
   }
 
-  auto issue = [&](unsigned char *st, int kt) {
-    const int koff = kt * SBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(ap[i] + koff, (lds_void *)(st + (wave * 4 + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(bp[i] + koff, (lds_void *)(st + A_BYTES + (wave * 4 + i) * 1024),
-                                       16, 0, 0);
-  };
-
-  // Fragment offsets: row = base + (lane & 31), logical chunk kk*2 + lane/32,
-  // swizzle term depends on lane bits 2..3 only.
   const int sw = (lane >> 2) & 3;
   const int fo0 = (lane & 31) * 64 + (((0 + (lane >> 5)) ^ sw) << 4);
   const int fo1 = (lane & 31) * 64 + (((2 + (lane >> 5)) ^ sw) << 4);
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-  // Rows of this wave's half (<= 0: the wave's results are discarded).
-  const int rows_here = tl.nrows - wm * 128;
+  // Active 32-row blocks of this wave's half (wave-uniform).
+  int rows_here = tl.nrows - wm * 128;
+  rows_here = rows_here < 0 ? 0 : (rows_here > 128 ? 128 : rows_here);
+  const int nmi = __builtin_amdgcn_readfirstlane((rows_here + 31) >> 5);
   const int KT = K / SBK;
-
-  auto compute = [&](const unsigned char *st) {
-    const unsigned char *sa = st + wm * 128 * 64;
-    const unsigned char *sb = st + A_BYTES + wn * 128 * 64;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int fo = kk ? fo1 : fo0;
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) a[mi] = *reinterpret_cast<const bf16x8 *>(sa + mi * 32 * 64 + fo);
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) b[ni] = *reinterpret_cast<const bf16x8 *>(sb + ni * 32 * 64 + fo);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-    }
-  };
 
   // The previous item's stores and loads are complete before the ring refills.
   wait_vmcnt<0>();
   raw_barrier();
-  issue(ring[0], 0);
-  issue(ring[1], 1);
-  issue(ring[2], 2);
-  // Stage kt lives in ring slot kt % 4 (unrolled by 4 so every slot index is
-  // static).  Stage kt is complete once at most the two later stages (8
-  // loads each) are outstanding; after the barrier stage kt+3 refills the
-  // slot stage kt-1 used.
-  const int KG = KT / NSTAGE;  // K is a multiple of 4 stages
-  for (int j = 0; j < KG - 1; ++j) {
-    const int kt = j * NSTAGE;
-#pragma unroll
-    for (int s4 = 0; s4 < NSTAGE; ++s4) {
-      wait_vmcnt<16>();
-      raw_barrier();
-      issue(ring[(s4 + 3) & 3], kt + s4 + 3);
-      compute(ring[s4]);
-    }
+  switch (nmi) {
+    case 0: kloop<DUAL, 0>(ring, ap, bp, KT, wave, wm, wn, fo0, fo1, acc); break;
+    case 1: kloop<DUAL, 1>(ring, ap, bp, KT, wave, wm, wn, fo0, fo1, acc); break;
+    case 2: kloop<DUAL, 2>(ring, ap, bp, KT, wave, wm, wn, fo0, fo1, acc); break;
+    case 3: kloop<DUAL, 3>(ring, ap, bp, KT, wave, wm, wn, fo0, fo1, acc); break;
+    default: kloop<DUAL, 4>(ring, ap, bp, KT, wave, wm, wn, fo0, fo1, acc); break;
   }
-  wait_vmcnt<16>();
-  raw_barrier();
-  issue(ring[3], KT - 1);
-  compute(ring[0]);
-  wait_vmcnt<16>();
-  raw_barrier();
-  compute(ring[1]);
-  wait_vmcnt<8>();
-  raw_barrier();
-  compute(ring[2]);
-  wait_vmcnt<0>();
-  raw_barrier();
-  compute(ring[3]);
   // Every wave is done reading the ring before it is reused for the output.
   raw_barrier();
 
   const int row_lane = 4 * (lane >> 5);
   if (DUAL) {
     // H tile: 256 rows x 128 columns bf16 (256 bytes a row); rows 0..127 in
-    // ring slot 0, rows 128..255 in slot 1.
-    if (rows_here > 0) {
-      uint16_t *Ht = reinterpret_cast<uint16_t *>(wm ? ring[1] : ring[0]);
+    // slot 0, rows 128..255 in slot 1.
+    uint16_t *Ht = reinterpret_cast<uint16_t *>(wm ? ring.s[1] : ring.s[0]);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi) {
+      if (mi >= nmi) break;
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = mi * 32 + 8 * (r >> 2) + row_lane + (r & 3);
-            const int col = wn * 64 + ni * 32 + (lane & 31);
-            Ht[row * 128 + col] = f32_to_bf16(silu(acc[mi][ni][r]) * acc[mi][ni + 2][r]);
-          }
-    }
-    __syncthreads();
-    uint16_t *C = static_cast<uint16_t *>(shared ? g.C_shared : g.C_routed);
-#pragma unroll 4
-    for (int j = 0; j < 16; ++j) {
-      const int q = tid + 256 * j;
-      const int row = q >> 4, ch = q & 15;
-      const uint16_t *Ht = reinterpret_cast<const uint16_t *>(row < 128 ? ring[0] : ring[1]);
-      if (row < tl.nrows)
-        *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
-            *reinterpret_cast<const uint4 *>(Ht + (row & 127) * 128 + ch * 8);
-    }
-    __syncthreads();
-  } else {
-    // Output tile: 256 x 256 bf16 (512 bytes a row); rows 64*s .. 64*s+63 in
-    // ring slot s.
-    if (rows_here > 0) {
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        uint16_t *Ot = reinterpret_cast<uint16_t *>(ring[wm * 2 + (mi >> 1)]);
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = (mi & 1) * 32 + 8 * (r >> 2) + row_lane + (r & 3);
-            const int col = wn * 128 + ni * 32 + (lane & 31);
-            Ot[row * 256 + col] = f32_to_bf16(acc[mi][ni][r]);
-          }
+      for (int r = 0; r < 16; ++r) {
+        const int row = mi * 32 + 8 * (r >> 2) + row_lane + (r & 3);
+        const int col = wn * 32 + (lane & 31);
+        Ht[row * 128 + col] = f32_to_bf16(silu(acc[mi][0][r]) * acc[mi][1][r]);
       }
     }
     __syncthreads();
     uint16_t *C = static_cast<uint16_t *>(shared ? g.C_shared : g.C_routed);
 #pragma unroll 4
-    for (int j = 0; j < 32; ++j) {
-      const int q = tid + 256 * j;
+    for (int j = 0; j < 8; ++j) {
+      const int q = tid + NTHREADS * j;
+      const int row = q >> 4, ch = q & 15;
+      const uint16_t *H = reinterpret_cast<const uint16_t *>(row < 128 ? ring.s[0] : ring.s[1]);
+      if (row < tl.nrows)
+        *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
+            *reinterpret_cast<const uint4 *>(H + (row & 127) * 128 + ch * 8);
+    }
+    __syncthreads();
+  } else {
+    // Output tile: 256 x 256 bf16 (512 bytes a row); rows 64*s .. 64*s+63 in slot s.
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      if (mi >= nmi) break;
+      uint16_t *Ot = reinterpret_cast<uint16_t *>(
+          wm ? (mi < 2 ? ring.s[2] : ring.s[3]) : (mi < 2 ? ring.s[0] : ring.s[1]));
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = (mi & 1) * 32 + 8 * (r >> 2) + row_lane + (r & 3);
+          const int col = wn * 64 + ni * 32 + (lane & 31);
+          Ot[row * 256 + col] = f32_to_bf16(acc[mi][ni][r]);
+        }
+    }
+    __syncthreads();
+    uint16_t *C = static_cast<uint16_t *>(shared ? g.C_shared : g.C_routed);
+#pragma unroll 4
+    for (int j = 0; j < 16; ++j) {
+      const int q = tid + NTHREADS * j;
       const int row = q >> 5, ch = q & 31;
-      const unsigned char *slot = row < 128 ? (row < 64 ? ring[0] : ring[1]) : (row < 192 ? ring[2] : ring[3]);
+      const unsigned char *slot =
+          row < 128 ? (row < 64 ? ring.s[0] : ring.s[1]) : (row < 192 ? ring.s[2] : ring.s[3]);
       if (row < tl.nrows)
         *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
             *reinterpret_cast<const uint4 *>(slot + (row & 63) * 512 + ch * 16);
@@ -263,7 +263,7 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, unsigne
 }
 
 template <bool DUAL>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_stream(StreamArgs g) {
+__global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_stream(StreamArgs g) {
   // Four separate ring slots: the compiler can then tell the LDS loads into
   // one slot from the reads of another and adds no waits of its own.
   __shared__ __attribute__((aligned(16))) unsigned char ring0[STAGE_BYTES];
@@ -271,6 +271,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_stream(StreamArgs g) {
   __shared__ __attribute__((aligned(16))) unsigned char ring2[STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char ring3[STAGE_BYTES];
   __shared__ int item_sh;
+  Ring ring;
+  ring.s[0] = ring0;
+  ring.s[1] = ring1;
+  ring.s[2] = ring2;
+  ring.s[3] = ring3;
   const int xcd = blockIdx.x & 7;
   for (int o = 0; o < 8; ++o) {
     const int x = (xcd + o) & 7;
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_stream(StreamArgs g) {
       const int it = item_sh;
       __syncthreads();
       if (it >= cnt) break;
-      run_item<DUAL>(g, g.items[off + it], ring0, ring1, ring2, ring3);
+      run_item<DUAL>(g, g.items[off + it], ring);
     }
   }
 }
@@ -442,7 +447,7 @@ hipError_t launch_stream_gate_up(const Plan &p, const void *u, const void *W1, c
   a.K_shared = c.d;
   a.C_routed = p.H;
   a.C_shared = p.Hs;
-  hipLaunchKernelGGL(grouped_gemm_stream<true>, dim3(num_cus()), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(grouped_gemm_stream<true>, dim3(num_cus()), dim3(NTHREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -462,7 +467,7 @@ hipError_t launch_stream_down(const Plan &p, const void *W2, const void *W2s, hi
   a.K_shared = c.F_shared;
   a.C_routed = p.O;
   a.C_shared = p.Z;
-  hipLaunchKernelGGL(grouped_gemm_stream<false>, dim3(num_cus()), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(grouped_gemm_stream<false>, dim3(num_cus()), dim3(NTHREADS), 0, s, a);
   return hipGetLastError();
 }
 

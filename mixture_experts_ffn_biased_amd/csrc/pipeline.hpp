@@ -1,0 +1,36 @@
+// Helpers for gfx950 kernels that stage tiles through LDS with direct
+// global-to-LDS loads (global_load_lds_dwordx4) in a ring of separate
+// __shared__ slots.  The wait counts are explicit: a stage is complete once
+// at most the loads issued after it are outstanding (loads complete in
+// order), and the barrier is a bare s_barrier, which does not wait for the
+// in-flight LDS loads the way __syncthreads() does.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace moe {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that neither waits for the in-flight LDS loads nor lets
+// the compiler move memory accesses across it.
+__device__ __forceinline__ void raw_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// 16 bytes per lane from global memory into LDS at lds + lane * 16.
+__device__ __forceinline__ void dma16(const void *src, void *lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 16, 0, 0);
+}
+
+}  // namespace moe

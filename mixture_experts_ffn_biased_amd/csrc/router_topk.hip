@@ -6,6 +6,11 @@
 // u_t^T e_i).  bf16 inputs use the bf16 MFMA (products of bf16 values are
 // exact in fp32); fp32 inputs use fp32 FMA.
 //
+// bf16 layers with d a multiple of 128 run router_topk_stream: 64 tokens per
+// workgroup, tiles of the tokens and of all router rows staged through a
+// 4-slot LDS ring by direct global-to-LDS loads (three stages in flight).
+// Other layers run router_topk_bf16 / router_topk_f32 (register staging).
+//
 // Selection ("The router in code"; "Sparse MoE FFN", "How it works",
 // Routing): s = l (softmax mode) or sigmoid(l); sb = s + bias; with groups,
 // group score = sum of the two largest sb, keep the topk_groups best groups;
@@ -13,6 +18,7 @@
 // NaN last.  Gates come from the raw scores: softmax over the chosen logits,
 // or s / sum(s) over the chosen, times route_scale.
 #include "common.hpp"
+#include "pipeline.hpp"
 #include "plan.hpp"
 
 namespace moe {
@@ -241,12 +247,154 @@ __global__ __launch_bounds__(256) void router_topk_f32(
   }
 }
 
+
+// ---- streamed router for bf16, d % 128 == 0 -----------------------------------
+
+constexpr int kRowsS = 64;  // tokens per workgroup
+
+// NB = experts / 64 rounded up (1..4): B tile of 64*NB router rows.
+template <int NB>
+__global__ __launch_bounds__(256, 1) void router_topk_stream(
+    const uint16_t *__restrict__ u, const uint16_t *__restrict__ Wr, int64_t T, int d, SelArgs sel,
+    int32_t *__restrict__ topk_idx, float *__restrict__ gates) {
+  constexpr int A_B = kRowsS * 64;         // 64 rows x 32 bf16
+  constexpr int B_B = NB * 64 * 64;        // 64*NB rows x 32 bf16
+  constexpr int SLOT = A_B + B_B;
+  constexpr int PER_STAGE = 1 + NB;        // DMA instructions per wave per stage
+  __shared__ __attribute__((aligned(16))) unsigned char ring0[SLOT];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[SLOT];
+  __shared__ __attribute__((aligned(16))) unsigned char ring2[SLOT];
+  __shared__ __attribute__((aligned(16))) unsigned char ring3[SLOT];
+  __shared__ float lg[kRowsS * kLogitStride];
+  unsigned char *const ring[4] = {ring0, ring1, ring2, ring3};
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRowsS;
+  const int E = sel.E;
+
+  // DMA sources: group g of 16 rows lands at g*1024 (A) or A_B + g*1024 (B);
+  // lane l -> row +l/4, physical chunk l%4 = logical chunk ^ ((row>>2)&3).
+  const int sub = lane >> 2;
+  const uint16_t *ap;
+  {
+    const int r = wave * 16 + sub;
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    int64_t t = t0 + r;
+    if (t >= T) t = T - 1;
+    ap = u + t * d + c * 8;
+  }
+  const uint16_t *bp[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int r = (wave * NB + j) * 16 + sub;
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int e = r < E ? r : E - 1;
+    bp[j] = Wr + static_cast<int64_t>(e) * d + c * 8;
+  }
+  auto issue = [&](unsigned char *st, int kt) {
+    const int koff = kt * 32;
+    dma16(ap + koff, st + wave * 1024);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) dma16(bp[j] + koff, st + A_B + (wave * NB + j) * 1024);
+  };
+
+  const int sw = (lane >> 2) & 3;
+  const int fo0 = (lane & 31) * 64 + (((0 + (lane >> 5)) ^ sw) << 4);
+  const int fo1 = (lane & 31) * 64 + (((2 + (lane >> 5)) ^ sw) << 4);
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+  const int wcol = wave < NB ? wave : 0;  // waves past the experts compute a copy, never stored
+  auto compute = [&](const unsigned char *st) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int fo = kk ? fo1 : fo0;
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) a[mi] = *reinterpret_cast<const bf16x8 *>(st + mi * 2048 + fo);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        b[ni] = *reinterpret_cast<const bf16x8 *>(st + A_B + (wcol * 64 + ni * 32) * 64 + fo);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+  };
+
+  const int KT = d / 32;  // multiple of 4, >= 4
+  issue(ring[0], 0);
+  issue(ring[1], 1);
+  issue(ring[2], 2);
+  for (int j = 0; j < KT / 4 - 1; ++j) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      wait_vmcnt<2 * PER_STAGE>();
+      raw_barrier();
+      issue(ring[(s4 + 3) & 3], j * 4 + s4 + 3);
+      compute(ring[s4]);
+    }
+  }
+  wait_vmcnt<2 * PER_STAGE>();
+  raw_barrier();
+  issue(ring[3], KT - 1);
+  compute(ring[0]);
+  wait_vmcnt<2 * PER_STAGE>();
+  raw_barrier();
+  compute(ring[1]);
+  wait_vmcnt<PER_STAGE>();
+  raw_barrier();
+  compute(ring[2]);
+  wait_vmcnt<0>();
+  raw_barrier();
+  compute(ring[3]);
+
+  if (wave < NB) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = wave * 64 + ni * 32 + (lane & 31);
+          if (col < E) lg[row * kLogitStride + col] = acc[mi][ni][r];
+        }
+  }
+  __syncthreads();
+  for (int row = wave; row < kRowsS; row += 4) {
+    const int64_t t = t0 + row;
+    if (t >= T) break;
+    select_token(lg + row * kLogitStride, sel, topk_idx + t * sel.k, gates + t * sel.k);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_router_topk(const Plan &p, const void *u, const void *Wr, const float *bias,
                               int32_t *topk_idx, float *gates, hipStream_t s) {
   const moe_cfg &c = p.cfg;
   SelArgs sel{c.E, c.k, c.score_fn, c.n_groups, c.topk_groups, c.route_scale, bias};
+  if (c.dtype == MOE_BF16 && c.d % 128 == 0) {
+    const dim3 grid(static_cast<unsigned>((c.T + kRowsS - 1) / kRowsS));
+    const int nb = (c.E + 63) / 64;
+    auto *U = static_cast<const uint16_t *>(u);
+    auto *W = static_cast<const uint16_t *>(Wr);
+    if (nb == 1)
+      hipLaunchKernelGGL(router_topk_stream<1>, grid, dim3(256), 0, s, U, W, c.T, c.d, sel, topk_idx, gates);
+    else if (nb == 2)
+      hipLaunchKernelGGL(router_topk_stream<2>, grid, dim3(256), 0, s, U, W, c.T, c.d, sel, topk_idx, gates);
+    else if (nb == 3)
+      hipLaunchKernelGGL(router_topk_stream<3>, grid, dim3(256), 0, s, U, W, c.T, c.d, sel, topk_idx, gates);
+    else
+      hipLaunchKernelGGL(router_topk_stream<4>, grid, dim3(256), 0, s, U, W, c.T, c.d, sel, topk_idx, gates);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>((c.T + kRows - 1) / kRows));
   if (c.dtype == MOE_BF16)
     hipLaunchKernelGGL(router_topk_bf16, grid, dim3(256), 0, s, static_cast<const uint16_t *>(u),
