@@ -119,6 +119,36 @@ moe_status moe_layer_forward(const void *u, const void *W_router, const float *b
                              size_t workspace_bytes, void *stream);
 
 /*
+ * Packed weights (bf16 layers with d, F and F_shared multiples of 256).
+ *
+ * The expert weights are static, so they may be re-laid out once (model
+ * load) into the order the streaming GEMM kernels consume them: for each
+ * expert, slabs of 256 weight rows (gate/up: 128 columns of W1 and the same
+ * 128 of W3, 32 rows of each alternating; down: 256 rows of W2), each slab as
+ * its K/32 stage blocks of 16 KiB, each block the 256 rows x 32 values in the
+ * order they land in LDS.  Every weight tile a kernel stage needs is then one
+ * contiguous 16 KiB read.  The computation is unchanged: moe_layer_forward
+ * and moe_layer_forward_packed give bitwise identical results.
+ *
+ * moe_packed_weights_bytes: size of the packed buffer for cfg's shapes (T is
+ *   ignored), or 0 when cfg cannot be packed.
+ * moe_pack_weights: fills packed (caller-owned device memory, >= that size,
+ *   16-byte aligned) from the plain W1, W3, W2 and shared weights of
+ *   moe_layer_forward; enqueued on stream.
+ * moe_layer_forward_packed: moe_layer_forward with the packed buffer in
+ *   place of W1, W3, W2 and shared (the shared expert is used iff
+ *   cfg->F_shared > 0).  Returns MOE_ERR_SHAPE when cfg cannot be packed or
+ *   T is too large for the streaming schedule.
+ */
+size_t moe_packed_weights_bytes(const moe_cfg *cfg);
+moe_status moe_pack_weights(const moe_cfg *cfg, const void *W1, const void *W3, const void *W2,
+                            const moe_shared *shared, void *packed, size_t packed_bytes, void *stream);
+moe_status moe_layer_forward_packed(const void *u, const void *W_router, const float *bias,
+                                    const void *packed, const moe_cfg *cfg, void *y, int32_t *topk_idx,
+                                    float *gates, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/*
  * Routing and permutation only (the first two stages of moe_layer_forward,
  * same kernels), for tests and tools.  Outputs, all int32 device arrays:
  *   counts [E]       slots that chose expert e
@@ -136,9 +166,11 @@ moe_status moe_route_debug(const void *u, const void *W_router, const float *bia
 /*
  * Which grouped-GEMM kernels moe_layer_forward uses for cfg (host only, no
  * GPU call): *gemm_path = 0 for the tiled kernels (any size, fp32 or bf16),
- * 1 for the persistent weight-streaming kernels (bf16, d % 256 == 0,
- * F % 128 == 0, F_shared % 128 == 0, at least 64 routed rows per expert on
- * average); *tile_rows = rows per GEMM tile.  Either pointer may be NULL.
+ * 1 for the persistent weight-streaming kernels with 256-row tiles (bf16,
+ * d % 256 == 0, F % 128 == 0, F_shared % 128 == 0, at least 64 routed rows
+ * per expert on average), 2 for their decode variant with 32-row tiles
+ * (fewer rows per expert; also F % 256 == 0, F_shared % 256 == 0);
+ * *tile_rows = rows per GEMM tile.  Either pointer may be NULL.
  */
 moe_status moe_plan_describe(const moe_cfg *cfg, int32_t *gemm_path, int32_t *tile_rows);
 

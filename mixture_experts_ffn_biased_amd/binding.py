@@ -101,6 +101,12 @@ def lib():
         L.moe_layer_forward.restype = I32
         L.moe_route_debug.argtypes = [P, P, P, CP, P, P, P, P, P, P, P, SZ, P]
         L.moe_route_debug.restype = I32
+        L.moe_packed_weights_bytes.argtypes = [CP]
+        L.moe_packed_weights_bytes.restype = SZ
+        L.moe_pack_weights.argtypes = [CP, P, P, P, ctypes.POINTER(moe_shared), P, SZ, P]
+        L.moe_pack_weights.restype = I32
+        L.moe_layer_forward_packed.argtypes = [P, P, P, P, CP, P, P, P, P, SZ, P]
+        L.moe_layer_forward_packed.restype = I32
         L.moe_plan_describe.argtypes = [CP, ctypes.POINTER(ctypes.c_int32),
                                         ctypes.POINTER(ctypes.c_int32)]
         L.moe_plan_describe.restype = I32
@@ -123,7 +129,7 @@ def moe_check_cfg(cfg: MoeConfig) -> int:
     return int(lib().moe_check_cfg(ctypes.byref(c)))
 
 
-GEMM_PATHS = {0: "tiled", 1: "stream"}
+GEMM_PATHS = {0: "tiled", 1: "stream", 2: "stream_decode"}
 
 
 def moe_plan_describe(cfg: MoeConfig):
@@ -210,6 +216,72 @@ def moe_layer_forward(u, W_router, bias, W1, W3, W2, shared: Optional[Sequence] 
                                  workspace.numel(), _stream(dev, stream))
     if st != 0:
         raise MoeError(st, "moe_layer_forward")
+    return y, topk_idx, gates
+
+
+def moe_packed_weights_bytes(cfg: MoeConfig) -> int:
+    c = cfg.to_c()
+    return int(lib().moe_packed_weights_bytes(ctypes.byref(c)))
+
+
+def moe_pack_weights(W1, W3, W2, shared: Optional[Sequence] = None, *, cfg: MoeConfig,
+                     packed=None, stream=None):
+    """One-time re-layout of the expert weights; returns the packed uint8 buffer."""
+    dev = W1.device
+    dt = cfg.torch_dtype
+    E, d, F, Fs = cfg.E, cfg.d, cfg.F, cfg.F_shared
+    _need(W1, (E, F, d), dt, "W1", dev)
+    _need(W3, (E, F, d), dt, "W3", dev)
+    _need(W2, (E, d, F), dt, "W2", dev)
+    sh = None
+    if shared is not None:
+        W1s, W3s, W2s = shared
+        _need(W1s, (Fs, d), dt, "W1s", dev)
+        _need(W3s, (Fs, d), dt, "W3s", dev)
+        _need(W2s, (d, Fs), dt, "W2s", dev)
+        sh = moe_shared(W1s.data_ptr(), W3s.data_ptr(), W2s.data_ptr())
+    n = moe_packed_weights_bytes(cfg)
+    if n == 0:
+        raise MoeError(-2, "moe_packed_weights_bytes")
+    if packed is None:
+        packed = torch.empty(n, dtype=torch.uint8, device=dev)
+    c = cfg.to_c()
+    st = lib().moe_pack_weights(ctypes.byref(c), _ptr(W1), _ptr(W3), _ptr(W2),
+                                ctypes.byref(sh) if sh is not None else None, _ptr(packed),
+                                packed.numel(), _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_pack_weights")
+    return packed
+
+
+def moe_layer_forward_packed(u, W_router, bias, packed, *, cfg: MoeConfig, y=None, topk_idx=None,
+                             gates=None, workspace=None, stream=None):
+    """moe_layer_forward with weights from moe_pack_weights."""
+    dev = u.device
+    dt = cfg.torch_dtype
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    _need(u, (T, d), dt, "u", dev)
+    _need(W_router, (E, d), dt, "W_router", dev)
+    if bias is not None:
+        _need(bias, (E,), torch.float32, "bias", dev)
+    _need(packed, (moe_packed_weights_bytes(cfg),), torch.uint8, "packed", dev)
+    if y is None:
+        y = torch.empty((T, d), dtype=dt, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if gates is None:
+        gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(y, (T, d), dt, "y", dev)
+    _need(topk_idx, (T, k), torch.int32, "topk_idx", dev)
+    _need(gates, (T, k), torch.float32, "gates", dev)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, dev)
+    c = cfg.to_c()
+    st = lib().moe_layer_forward_packed(_ptr(u), _ptr(W_router), _ptr(bias), _ptr(packed),
+                                        ctypes.byref(c), _ptr(y), _ptr(topk_idx), _ptr(gates),
+                                        _ptr(workspace), workspace.numel(), _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_layer_forward_packed")
     return y, topk_idx, gates
 
 

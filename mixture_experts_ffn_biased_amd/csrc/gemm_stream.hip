@@ -1,30 +1,37 @@
-// Grouped expert GEMMs for prefill-sized groups (many rows per expert): a
-// persistent, XCD-aware, weight-streaming kernel for gfx950.
+// Grouped expert GEMMs on gfx950 for bf16 layers: persistent, XCD-aware,
+// weight-streaming kernels.
 //
 // Same two products as grouped_gemm.hip (the SwiGLU expert of "Sparse MoE
 // FFN" (DeepSeek-V3), "How it works", batched as grouped GEMMs as "Mixture of
 // experts and architecture families", "The router and load balancing",
 // suggests); only the schedule and the data movement differ:
 //
-//  * One 512-thread workgroup per CU loops over work items (tile, n-slab).
-//    Items are kept in eight per-XCD lists: a chunk (up to two 256-row tiles
-//    of one expert) goes to one XCD with all its n-slabs, the tiles of a
-//    chunk adjacent.  Workgroups of an XCD take items from their list in
-//    order through an atomic counter, so the workgroups running together on
-//    an XCD share the expert's token rows and weight slabs in that XCD's L2,
-//    and each weight byte is fetched from HBM about once.  A workgroup whose
-//    list is empty takes items from the other XCDs' lists.
-//  * Tiles of 256 rows x 256 weight rows x 32, staged by direct global-to-LDS
-//    16-byte loads (global_load_lds_dwordx4) through a 4-stage ring, so three
-//    stages (96 KB) are in flight while one is multiplied; no VGPR staging.
-//  * Eight waves in a 2x4 grid (two per SIMD, one from each row half), each
-//    128 x 64 of v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  A wave
-//    multiplies only the 32-row blocks that hold rows of the tile (its K loop
-//    is specialised on that count), so a SIMD's MFMA work follows the tile's
-//    row count, and each SIMD has a second wave to cover waits.
-//  * gate_up: the 256 weight rows of a slab are 32 rows of W1 then the same
-//    32 of W3 per wave column, so SiLU(x W1^T) * (x W3^T) meets in the same
-//    lane; the bf16 result goes through LDS to 16-byte stores.
+//  * One workgroup per CU loops over work items (tile, n-slab).  Items are
+//    kept in eight per-XCD lists: a chunk (up to two tiles of one expert)
+//    goes to one XCD with all its n-slabs, the tiles of a chunk adjacent.
+//    Workgroups of an XCD take items from their list in order through an
+//    atomic counter, so the workgroups running together on an XCD share the
+//    expert's token rows and weight slabs in that XCD's L2, and each weight
+//    byte is fetched from HBM about once.  A workgroup whose list is empty
+//    takes items from the other XCDs' lists.
+//  * Each stage is a K-slice of 32: the tile's token rows and 256 weight rows,
+//    staged by direct global-to-LDS 16-byte loads (global_load_lds_dwordx4)
+//    through a ring of LDS slots; all but one slot are in flight while one is
+//    multiplied; no VGPR staging.
+//  * Prefill variant: 256-row tiles, 8 waves in a 2x4 grid (two per SIMD, one
+//    from each row half), each 128 x 64 of v_mfma_f32_32x32x16_bf16 with fp32
+//    accumulators, a 4-slot ring (96 KB in flight).  A wave multiplies only
+//    the 32-row blocks that hold rows of the tile (its K loop is specialised
+//    on that count), so a SIMD's MFMA work follows the tile's row count.
+//  * Decode variant (few rows per expert): 32-row tiles, 4 waves each 32 x 64,
+//    an 8-slot ring (7 x 16 KB of weights in flight): a weight stream with a
+//    small MFMA on the side.
+//  * gate_up: each wave column's 64 weight rows are 32 rows of W1 then the
+//    same 32 of W3, so SiLU(x W1^T) * (x W3^T) meets in the same lane; the
+//    bf16 result goes through LDS to 16-byte stores.
+//  * Weights are read either in their plain [rows][K] layout or packed once
+//    (moe_pack_weights) so that each stage's 16 KB weight tile is contiguous
+//    in memory in exactly the order it lands in LDS.
 #include "common.hpp"
 #include "pipeline.hpp"
 #include "plan.hpp"
@@ -32,11 +39,25 @@
 namespace moe {
 namespace {
 
-constexpr int SBM = 256, SBN = 256, SBK = 32, NSTAGE = 4;
-constexpr int NTHREADS = 512;  // 8 waves: 2 row halves x 4 column quarters
-constexpr int A_BYTES = SBM * SBK * 2;
+constexpr int SBK = 32;            // K per stage
+constexpr int SBN = 256;           // weight rows per stage
 constexpr int B_BYTES = SBN * SBK * 2;
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int B_STAGE_ELEMS = SBN * SBK;  // packed: elements per weight stage block
+
+template <int VAR>
+struct V;
+template <>
+struct V<0> {  // prefill
+  static constexpr int BM = 256, NT = 512, NSTAGE = 4, A_LOADS = 2, B_LOADS = 2;
+};
+template <>
+struct V<1> {  // decode
+  static constexpr int BM = 32, NT = 256, NSTAGE = 8, A_LOADS = 1, B_LOADS = 4;
+};
+template <int VAR>
+constexpr int a_bytes() { return V<VAR>::BM * SBK * 2; }
+template <int VAR>
+constexpr int stage_bytes() { return a_bytes<VAR>() + B_BYTES; }
 
 struct StreamArgs {
   const Tile *tiles;
@@ -49,34 +70,69 @@ struct StreamArgs {
   int E;
   const void *A_routed, *A_shared;
   int gather;
-  const void *B0_routed, *B1_routed, *B0_shared, *B1_shared;
+  const void *B0_routed, *B1_routed, *B0_shared, *B1_shared;  // plain layout
+  const void *Bp_routed, *Bp_shared;  // packed layout: stage blocks of each slab
   int N_routed, N_shared, K_routed, K_shared;
   void *C_routed, *C_shared;
 };
 
-// Ring slots of one workgroup (separate __shared__ arrays).
+template <int NS>
 struct Ring {
-  unsigned char *s[NSTAGE];
+  unsigned char *s[NS];
 };
 
-// The K loop of one item for a wave with NMI active 32-row blocks (0..4).
-// Every wave runs the same loads and barriers whatever its NMI, so waves
-// with different row counts stay in step.
-template <bool DUAL, int NMI>
-__device__ __forceinline__ void kloop(const Ring &ring, const uint16_t *const (&ap)[2],
-                                      const uint16_t *const (&bp)[2], int KT, int wave, int wm,
-                                      int wn, int fo0, int fo1, f32x16 (&acc)[4][2]) {
+template <int VAR>
+struct Ptrs {
+  const uint16_t *a[V<VAR>::A_LOADS];
+  const uint16_t *b[V<VAR>::B_LOADS];
+};
+
+// Wait for stage S of the last ring turn, barrier, multiply; then the next.
+template <int NS, int PS, int S>
+struct Tail {
+  template <class C>
+  __device__ __forceinline__ static void run(const Ring<NS> &ring, C &compute) {
+    wait_vmcnt<(NS - 1 - S) * PS>();
+    raw_barrier();
+    compute(ring.s[S]);
+    Tail<NS, PS, S + 1>::run(ring, compute);
+  }
+};
+template <int NS, int PS>
+struct Tail<NS, PS, NS> {
+  template <class C>
+  __device__ __forceinline__ static void run(const Ring<NS> &, C &) {}
+};
+
+// The K loop of one item for a wave with NMI active 32-row blocks.  Every
+// wave issues the same loads and barriers whatever its NMI, so waves with
+// different row counts stay in step.
+template <bool PACKED, int VAR, int NMI>
+__device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Ptrs<VAR> &p, int KT,
+                                      int wave, int lane, int wm, int wn, int fo0, int fo1,
+                                      f32x16 (&acc)[4][2]) {
+  constexpr int NS = V<VAR>::NSTAGE;
+  constexpr int PS = V<VAR>::A_LOADS + V<VAR>::B_LOADS;  // loads per wave per stage
+  constexpr int AB = a_bytes<VAR>();
   auto issue = [&](unsigned char *st, int kt) {
     const int koff = kt * SBK;
+    if (VAR == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(ap[i] + koff, st + (wave * 2 + i) * 1024);
+      for (int i = 0; i < V<VAR>::A_LOADS; ++i) dma16(p.a[i] + koff, st + (wave * 2 + i) * 1024);
+    } else {
+      // 32 rows: each wave loads 8 rows with its first 32 lanes.
+      if (lane < 32) dma16(p.a[0] + koff, st + wave * 512);
+    }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(bp[i] + koff, st + A_BYTES + (wave * 2 + i) * 1024);
+    for (int i = 0; i < V<VAR>::B_LOADS; ++i) {
+      const uint16_t *src = PACKED ? p.b[i] + static_cast<int64_t>(kt) * B_STAGE_ELEMS : p.b[i] + koff;
+      dma16(src, st + AB + (wave * V<VAR>::B_LOADS + i) * 1024);
+    }
   };
   auto compute = [&](const unsigned char *st) {
     if (NMI == 0) return;
     const unsigned char *sa = st + wm * 128 * 64;
-    const unsigned char *sb = st + A_BYTES + wn * 64 * 64;
+    const unsigned char *sb = st + AB + wn * 64 * 64;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int fo = kk ? fo1 : fo0;
@@ -92,84 +148,93 @@ __device__ __forceinline__ void kloop(const Ring &ring, const uint16_t *const (&
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
     }
   };
-  constexpr int PS = 2 * 2;  // loads per wave per stage
-  issue(ring.s[0], 0);
-  issue(ring.s[1], 1);
-  issue(ring.s[2], 2);
-  // Stage kt lives in slot kt % 4 (unrolled by 4: static slot indices).  It
-  // is complete once at most the two later stages are outstanding; after
-  // the barrier, stage kt+3 refills the slot of stage kt-1.
-  for (int j = 0; j < KT / NSTAGE - 1; ++j) {
 #pragma unroll
-    for (int s4 = 0; s4 < NSTAGE; ++s4) {
-      wait_vmcnt<2 * PS>();
+  for (int i = 0; i < NS - 1; ++i) issue(ring.s[i], i);
+  // Stage kt lives in slot kt % NS (unrolled: static slot indices).  It is
+  // complete once at most the NS-2 later stages are outstanding; after the
+  // barrier, stage kt+NS-1 refills the slot of stage kt-1.
+  for (int j = 0; j < KT / NS - 1; ++j) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      wait_vmcnt<(NS - 2) * PS>();
       raw_barrier();
-      issue(ring.s[(s4 + 3) & 3], j * NSTAGE + s4 + 3);
-      compute(ring.s[s4]);
+      issue(ring.s[(s + NS - 1) % NS], j * NS + s + NS - 1);
+      compute(ring.s[s]);
     }
   }
-  wait_vmcnt<2 * PS>();
+  wait_vmcnt<(NS - 2) * PS>();
   raw_barrier();
-  issue(ring.s[3], KT - 1);
+  issue(ring.s[NS - 1], KT - 1);
   compute(ring.s[0]);
-  wait_vmcnt<2 * PS>();
-  raw_barrier();
-  compute(ring.s[1]);
-  wait_vmcnt<PS>();
-  raw_barrier();
-  compute(ring.s[2]);
-  wait_vmcnt<0>();
-  raw_barrier();
-  compute(ring.s[3]);
+  Tail<NS, PS, 1>::run(ring, compute);
 }
 
-template <bool DUAL>
-__device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const Ring &ring) {
+template <bool DUAL, bool PACKED, int VAR>
+__device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const Ring<V<VAR>::NSTAGE> &ring) {
+  constexpr int BM = V<VAR>::BM, NT = V<VAR>::NT;
   const Tile tl = g.tiles[item.x];
   const bool shared = tl.group == g.E;
   const int N = shared ? g.N_shared : g.N_routed;
   const int K = shared ? g.K_shared : g.K_routed;
+  const int KT = K / SBK;
   const int n0 = item.y * (DUAL ? SBN / 2 : SBN);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = VAR == 0 ? wave >> 2 : 0, wn = VAR == 0 ? (wave & 3) : wave;
 
   const uint16_t *A = static_cast<const uint16_t *>(shared ? g.A_shared : g.A_routed);
-  const uint16_t *B0 = static_cast<const uint16_t *>(shared ? g.B0_shared : g.B0_routed);
-  const uint16_t *B1 = static_cast<const uint16_t *>(shared ? g.B1_shared : g.B1_routed);
-  if (!shared) {
-    const int64_t es = static_cast<int64_t>(N) * K;
-    B0 += tl.group * es;
-    if (DUAL) B1 += tl.group * es;
-  }
-
-  // DMA sources: load i of wave w fills LDS rows g*16 .. g*16+15 (g = 2w+i)
-  // of the A and B tiles; lane l lands in row +l/4, physical chunk l%4,
-  // which holds logical k-chunk (l%4) ^ ((row>>2)&3).  Rows past the tile's
-  // count read its first row (never stored).
-  const uint16_t *ap[2];
-  const uint16_t *bp[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (wave * 2 + i) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
-    const int rr = r < tl.nrows ? r : 0;
+  auto a_row = [&](int r) -> const uint16_t * {
+    const int rr = r < tl.nrows ? r : 0;  // rows past the count read row 0 (never stored)
     int64_t arow;
     if (g.gather && !shared)
       arow = g.perm[tl.row0 + rr] / g.k;
     else
       arow = static_cast<int64_t>(tl.row0) + rr;
-    ap[i] = A + arow * K + c * 8;
-    int64_t brow;
-    const uint16_t *bsrc = B0;
-    if (DUAL) {
-      // 64 rows per wave column: 32 of W1, then the same 32 of W3.
-      const int q = r & 63;
-      brow = n0 + (r >> 6) * 32 + (q & 31);
-      if (q >= 32) bsrc = B1;
-    } else {
-      brow = n0 + r;
+    return A + arow * K;
+  };
+
+  // DMA sources.  A load fills 16 LDS rows (8 in the decode variant, first
+  // 32 lanes); lane l lands in row +l/4, physical chunk l%4, which holds
+  // logical k-chunk (l%4) ^ ((row>>2)&3).
+  Ptrs<VAR> p;
+#pragma unroll
+  for (int i = 0; i < V<VAR>::A_LOADS; ++i) {
+    const int r = VAR == 0 ? (wave * 2 + i) * 16 + (lane >> 2) : wave * 8 + ((lane & 31) >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    p.a[i] = a_row(r) + c * 8;
+  }
+  if (PACKED) {
+    // The slab's stage blocks are contiguous: block kt at kt * B_STAGE_ELEMS,
+    // load i of wave w at (w * B_LOADS + i) KiB in the block, lane at 16 B.
+    const uint16_t *Bp = static_cast<const uint16_t *>(shared ? g.Bp_shared : g.Bp_routed);
+    const int nslab = DUAL ? N / (SBN / 2) : N / SBN;
+    const int64_t slab = (shared ? 0 : static_cast<int64_t>(tl.group) * nslab) + item.y;
+    const uint16_t *blk = Bp + slab * KT * B_STAGE_ELEMS;
+#pragma unroll
+    for (int i = 0; i < V<VAR>::B_LOADS; ++i) p.b[i] = blk + (wave * V<VAR>::B_LOADS + i) * 512 + lane * 8;
+  } else {
+    const uint16_t *B0 = static_cast<const uint16_t *>(shared ? g.B0_shared : g.B0_routed);
+    const uint16_t *B1 = static_cast<const uint16_t *>(shared ? g.B1_shared : g.B1_routed);
+    if (!shared) {
+      const int64_t es = static_cast<int64_t>(N) * K;
+      B0 += tl.group * es;
+      if (DUAL) B1 += tl.group * es;
     }
-    bp[i] = bsrc + brow * K + c * 8;
+#pragma unroll
+    for (int i = 0; i < V<VAR>::B_LOADS; ++i) {
+      const int r = (wave * V<VAR>::B_LOADS + i) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      int64_t brow;
+      const uint16_t *bsrc = B0;
+      if (DUAL) {
+        // 64 rows per wave column: 32 of W1, then the same 32 of W3.
+        const int q = r & 63;
+        brow = n0 + (r >> 6) * 32 + (q & 31);
+        if (q >= 32) bsrc = B1;
+      } else {
+        brow = n0 + r;
+      }
+      p.b[i] = bsrc + brow * K + c * 8;
+    }
   }
 
   const int sw = (lane >> 2) & 3;
@@ -187,25 +252,29 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   // Active 32-row blocks of this wave's half (wave-uniform).
   int rows_here = tl.nrows - wm * 128;
   rows_here = rows_here < 0 ? 0 : (rows_here > 128 ? 128 : rows_here);
-  const int nmi = __builtin_amdgcn_readfirstlane((rows_here + 31) >> 5);
-  const int KT = K / SBK;
+  const int nmi = VAR == 0 ? __builtin_amdgcn_readfirstlane((rows_here + 31) >> 5) : 1;
 
   // The previous item's stores and loads are complete before the ring refills.
   wait_vmcnt<0>();
   raw_barrier();
-  switch (nmi) {
-    case 0: kloop<DUAL, 0>(ring, ap, bp, KT, wave, wm, wn, fo0, fo1, acc); break;
-    case 1: kloop<DUAL, 1>(ring, ap, bp, KT, wave, wm, wn, fo0, fo1, acc); break;
-    case 2: kloop<DUAL, 2>(ring, ap, bp, KT, wave, wm, wn, fo0, fo1, acc); break;
-    case 3: kloop<DUAL, 3>(ring, ap, bp, KT, wave, wm, wn, fo0, fo1, acc); break;
-    default: kloop<DUAL, 4>(ring, ap, bp, KT, wave, wm, wn, fo0, fo1, acc); break;
+  if (VAR == 0) {
+    switch (nmi) {
+      case 0: kloop<PACKED, VAR, 0>(ring, p, KT, wave, lane, wm, wn, fo0, fo1, acc); break;
+      case 1: kloop<PACKED, VAR, 1>(ring, p, KT, wave, lane, wm, wn, fo0, fo1, acc); break;
+      case 2: kloop<PACKED, VAR, 2>(ring, p, KT, wave, lane, wm, wn, fo0, fo1, acc); break;
+      case 3: kloop<PACKED, VAR, 3>(ring, p, KT, wave, lane, wm, wn, fo0, fo1, acc); break;
+      default: kloop<PACKED, VAR, 4>(ring, p, KT, wave, lane, wm, wn, fo0, fo1, acc); break;
+    }
+  } else {
+    kloop<PACKED, VAR, 1>(ring, p, KT, wave, lane, wm, wn, fo0, fo1, acc);
   }
   // Every wave is done reading the ring before it is reused for the output.
   raw_barrier();
 
   const int row_lane = 4 * (lane >> 5);
+  uint16_t *C = static_cast<uint16_t *>(shared ? g.C_shared : g.C_routed);
   if (DUAL) {
-    // H tile: 256 rows x 128 columns bf16 (256 bytes a row); rows 0..127 in
+    // H tile: BM rows x 128 columns bf16 (256 bytes a row); rows 0..127 in
     // slot 0, rows 128..255 in slot 1.
     uint16_t *Ht = reinterpret_cast<uint16_t *>(wm ? ring.s[1] : ring.s[0]);
 #pragma unroll
@@ -219,10 +288,9 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
       }
     }
     __syncthreads();
-    uint16_t *C = static_cast<uint16_t *>(shared ? g.C_shared : g.C_routed);
 #pragma unroll 4
-    for (int j = 0; j < 8; ++j) {
-      const int q = tid + NTHREADS * j;
+    for (int j = 0; j < BM * 16 / NT; ++j) {
+      const int q = tid + NT * j;
       const int row = q >> 4, ch = q & 15;
       const uint16_t *H = reinterpret_cast<const uint16_t *>(row < 128 ? ring.s[0] : ring.s[1]);
       if (row < tl.nrows)
@@ -231,7 +299,8 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
     }
     __syncthreads();
   } else {
-    // Output tile: 256 x 256 bf16 (512 bytes a row); rows 64*s .. 64*s+63 in slot s.
+    // Output tile: BM x 256 bf16 (512 bytes a row); rows 64*s .. 64*s+63 in
+    // slot s (the decode tile's 32 rows all in slot 0).
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       if (mi >= nmi) break;
@@ -247,10 +316,9 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
         }
     }
     __syncthreads();
-    uint16_t *C = static_cast<uint16_t *>(shared ? g.C_shared : g.C_routed);
 #pragma unroll 4
-    for (int j = 0; j < 16; ++j) {
-      const int q = tid + NTHREADS * j;
+    for (int j = 0; j < BM * 32 / NT; ++j) {
+      const int q = tid + NT * j;
       const int row = q >> 5, ch = q & 31;
       const unsigned char *slot =
           row < 128 ? (row < 64 ? ring.s[0] : ring.s[1]) : (row < 192 ? ring.s[2] : ring.s[3]);
@@ -262,33 +330,96 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   }
 }
 
-template <bool DUAL>
-__global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_stream(StreamArgs g) {
-  // Four separate ring slots: the compiler can then tell the LDS loads into
-  // one slot from the reads of another and adds no waits of its own.
-  __shared__ __attribute__((aligned(16))) unsigned char ring0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char ring1[STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char ring2[STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char ring3[STAGE_BYTES];
-  __shared__ int item_sh;
-  Ring ring;
-  ring.s[0] = ring0;
-  ring.s[1] = ring1;
-  ring.s[2] = ring2;
-  ring.s[3] = ring3;
+template <bool DUAL, bool PACKED, int VAR>
+__device__ __forceinline__ void item_loop(const StreamArgs &g, const Ring<V<VAR>::NSTAGE> &ring,
+                                          int *item_sh) {
   const int xcd = blockIdx.x & 7;
   for (int o = 0; o < 8; ++o) {
     const int x = (xcd + o) & 7;
     const int cnt = g.xcd_cnt[x];
     const int off = g.xcd_off[x];
     for (;;) {
-      if (threadIdx.x == 0) item_sh = atomicAdd(&g.counters[x], 1);
+      if (threadIdx.x == 0) *item_sh = atomicAdd(&g.counters[x], 1);
       __syncthreads();
-      const int it = item_sh;
+      const int it = *item_sh;
       __syncthreads();
       if (it >= cnt) break;
-      run_item<DUAL>(g, g.items[off + it], ring);
+      run_item<DUAL, PACKED, VAR>(g, g.items[off + it], ring);
     }
+  }
+}
+
+// Separate __shared__ ring slots: the compiler can then tell the LDS loads
+// into one slot from the reads of another and adds no waits of its own.
+template <bool DUAL, bool PACKED>
+__global__ __launch_bounds__(512, 1) void gemm_stream_prefill(StreamArgs g) {
+  constexpr int SB = stage_bytes<0>();
+  __shared__ __attribute__((aligned(16))) unsigned char r0[SB], r1[SB], r2[SB], r3[SB];
+  __shared__ int item_sh;
+  Ring<4> ring;
+  ring.s[0] = r0;
+  ring.s[1] = r1;
+  ring.s[2] = r2;
+  ring.s[3] = r3;
+  item_loop<DUAL, PACKED, 0>(g, ring, &item_sh);
+}
+
+template <bool DUAL, bool PACKED>
+__global__ __launch_bounds__(256, 1) void gemm_stream_decode(StreamArgs g) {
+  constexpr int SB = stage_bytes<1>();
+  __shared__ __attribute__((aligned(16))) unsigned char r0[SB], r1[SB], r2[SB], r3[SB], r4[SB], r5[SB],
+      r6[SB], r7[SB];
+  __shared__ int item_sh;
+  Ring<8> ring;
+  ring.s[0] = r0;
+  ring.s[1] = r1;
+  ring.s[2] = r2;
+  ring.s[3] = r3;
+  ring.s[4] = r4;
+  ring.s[5] = r5;
+  ring.s[6] = r6;
+  ring.s[7] = r7;
+  item_loop<DUAL, PACKED, 1>(g, ring, &item_sh);
+}
+
+// ---- one-time weight packing -------------------------------------------------
+
+// Packed layout, for one matrix kind (gate_up: W1 and W3 together; down: W2)
+// of one expert: slabs of 256 weight rows in order, each slab its K/32 stage
+// blocks in order, each block 256 rows x 64 bytes exactly as the rows land in
+// LDS: row r, physical 16-byte chunk p holds k-chunk p ^ ((r>>2)&3) of the
+// K-slice; for gate_up, row r is W1 row slab*128 + (r/64)*32 + r%32 when
+// r%64 < 32 and the same row of W3 otherwise.
+__global__ __launch_bounds__(256) void pack_weights(const uint16_t *__restrict__ W1,
+                                                    const uint16_t *__restrict__ W3, int dual,
+                                                    int64_t n_mats, int rows, int K,
+                                                    uint16_t *__restrict__ out) {
+  const int KT = K / SBK;
+  const int nslab = dual ? rows / (SBN / 2) : rows / SBN;
+  const int64_t per_mat = static_cast<int64_t>(nslab) * KT * (B_BYTES / 16);
+  const int64_t total = n_mats * per_mat;
+  for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < total;
+       q += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t e = q / per_mat;
+    int64_t rem = q - e * per_mat;
+    const int chunk = static_cast<int>(rem % (B_BYTES / 16));  // 16-byte chunk in the block
+    rem /= (B_BYTES / 16);
+    const int kt = static_cast<int>(rem % KT);
+    const int slab = static_cast<int>(rem / KT);
+    const int r = chunk >> 2, pch = chunk & 3;
+    const int c = pch ^ ((r >> 2) & 3);
+    const uint16_t *src;
+    int64_t row;
+    if (dual) {
+      const int qq = r & 63;
+      row = static_cast<int64_t>(slab) * 128 + (r >> 6) * 32 + (qq & 31);
+      src = qq < 32 ? W1 : W3;
+    } else {
+      row = static_cast<int64_t>(slab) * SBN + r;
+      src = W1;
+    }
+    const uint16_t *from = src + (e * rows + row) * K + kt * SBK + c * 8;
+    *reinterpret_cast<uint4 *>(out + q * 8) = *reinterpret_cast<const uint4 *>(from);
   }
 }
 
@@ -297,11 +428,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_gemm_stream(StreamArgs g)
 constexpr int kMaxChunks = 4096;
 
 // One block.  Rebuilds the tile numbering of perm_scan (experts in order,
-// ceil(count/256) tiles each, then the shared expert's tiles), groups tiles
+// ceil(count/tile_m) tiles each, then the shared expert's tiles), groups tiles
 // into chunks of up to two per expert, deals chunks to XCDs round-robin and
 // writes both GEMMs' item lists (tile fastest, then n-slab, within a chunk).
 __global__ __launch_bounds__(256) void stream_schedule(
-    const int32_t *__restrict__ counts, int E, int64_t T, int has_shared, int nt_gu_r, int nt_gu_s,
+    const int32_t *__restrict__ counts, int E, int64_t T, int has_shared, int tile_m, int nt_gu_r,
+    int nt_gu_s,
     int nt_dn_r, int nt_dn_s, int2 *__restrict__ items_gu, int2 *__restrict__ items_dn,
     int32_t *__restrict__ meta /* [2][3][8]: off, cnt, counter for gate_up, down */) {
   __shared__ int cfirst[kMaxChunks];
@@ -313,7 +445,7 @@ __global__ __launch_bounds__(256) void stream_schedule(
   const int tid = threadIdx.x;
   const int e = tid;
   const int c = e < E ? counts[e] : 0;
-  const int nt = (c + SBM - 1) / SBM;
+  const int nt = (c + tile_m - 1) / tile_m;
   const int nch = (nt + 1) / 2;
   // exclusive scans of tiles and chunks
   buf[tid] = nt;
@@ -344,7 +476,7 @@ __global__ __launch_bounds__(256) void stream_schedule(
   }
   int n_chunks = routed_chunks;
   if (has_shared) {
-    const int ns = static_cast<int>((T + SBM - 1) / SBM);
+    const int ns = static_cast<int>((T + tile_m - 1) / tile_m);
     const int nsc = (ns + 1) / 2;
     for (int j = tid; j < nsc; j += 256) {
       cfirst[routed_chunks + j] = routed_tiles + 2 * j;
@@ -417,21 +549,72 @@ StreamArgs base_args(const Plan &p, int list) {
 
 }  // namespace
 
-int stream_tile_m() { return SBM; }
+int stream_tile_m(int path) { return path == PATH_STREAM_DECODE ? V<1>::BM : V<0>::BM; }
 int stream_max_chunks() { return kMaxChunks; }
 int stream_nslab_gate_up(int F) { return F / (SBN / 2); }
 int stream_nslab_down(int d) { return d / SBN; }
 
+size_t packed_weights_bytes(const moe_cfg &c) {
+  return 2ull * (2ull * c.E * c.F * c.d + static_cast<size_t>(c.E) * c.d * c.F + 2ull * c.F_shared * c.d +
+                 static_cast<size_t>(c.d) * c.F_shared);
+}
+
+PackedView packed_view(const moe_cfg &c, const void *base) {
+  const char *b = static_cast<const char *>(base);
+  PackedView v;
+  v.gu = b;
+  v.dn = b + 4ull * c.E * c.F * c.d;
+  v.gu_s = static_cast<const char *>(v.dn) + 2ull * c.E * c.d * c.F;
+  v.dn_s = static_cast<const char *>(v.gu_s) + 4ull * c.F_shared * c.d;
+  return v;
+}
+
+hipError_t launch_pack_weights(const moe_cfg &c, const void *W1, const void *W3, const void *W2,
+                               const void *W1s, const void *W3s, const void *W2s, void *packed,
+                               hipStream_t s) {
+  const PackedView v = packed_view(c, packed);
+  auto run = [&](const void *a, const void *b, int dual, int64_t n, int rows, int K, const void *out) {
+    const int64_t chunks = n * static_cast<int64_t>(rows) * K * (dual ? 2 : 1) / 8;
+    const unsigned blocks = static_cast<unsigned>(chunks / 256 < 65536 ? (chunks + 255) / 256 : 65536);
+    hipLaunchKernelGGL(pack_weights, dim3(blocks), dim3(256), 0, s, static_cast<const uint16_t *>(a),
+                       static_cast<const uint16_t *>(b), dual, n, rows, K,
+                       static_cast<uint16_t *>(const_cast<void *>(out)));
+    return hipGetLastError();
+  };
+  hipError_t e = run(W1, W3, 1, c.E, c.F, c.d, v.gu);
+  if (e == hipSuccess) e = run(W2, nullptr, 0, c.E, c.d, c.F, v.dn);
+  if (e == hipSuccess && c.F_shared > 0) e = run(W1s, W3s, 1, 1, c.F_shared, c.d, v.gu_s);
+  if (e == hipSuccess && c.F_shared > 0) e = run(W2s, nullptr, 0, 1, c.d, c.F_shared, v.dn_s);
+  return e;
+}
+
 hipError_t launch_stream_schedule(const Plan &p, hipStream_t s) {
   const moe_cfg &c = p.cfg;
   hipLaunchKernelGGL(stream_schedule, dim3(1), dim3(256), 0, s, p.counts, c.E, c.T, c.F_shared > 0 ? 1 : 0,
-                     c.F / (SBN / 2), c.F_shared / (SBN / 2), c.d / SBN, c.d / SBN, p.items_gu, p.items_dn,
-                     p.sched_meta);
+                     p.tile_m, c.F / (SBN / 2), c.F_shared / (SBN / 2), c.d / SBN, c.d / SBN, p.items_gu,
+                     p.items_dn, p.sched_meta);
+  return hipGetLastError();
+}
+
+static hipError_t launch_stream(const Plan &p, const StreamArgs &a, bool dual, bool packed, hipStream_t s) {
+  typedef void (*kernel_t)(StreamArgs);
+  kernel_t k;
+  int threads;
+  if (p.path == PATH_STREAM_DECODE) {
+    threads = V<1>::NT;
+    k = dual ? (packed ? gemm_stream_decode<true, true> : gemm_stream_decode<true, false>)
+             : (packed ? gemm_stream_decode<false, true> : gemm_stream_decode<false, false>);
+  } else {
+    threads = V<0>::NT;
+    k = dual ? (packed ? gemm_stream_prefill<true, true> : gemm_stream_prefill<true, false>)
+             : (packed ? gemm_stream_prefill<false, true> : gemm_stream_prefill<false, false>);
+  }
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(num_cus())), dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_stream_gate_up(const Plan &p, const void *u, const void *W1, const void *W3,
-                                 const void *W1s, const void *W3s, hipStream_t s) {
+                                 const void *W1s, const void *W3s, const PackedView *pk, hipStream_t s) {
   const moe_cfg &c = p.cfg;
   StreamArgs a = base_args(p, 0);
   a.A_routed = u;
@@ -441,17 +624,19 @@ hipError_t launch_stream_gate_up(const Plan &p, const void *u, const void *W1, c
   a.B1_routed = W3;
   a.B0_shared = W1s;
   a.B1_shared = W3s;
+  a.Bp_routed = pk ? pk->gu : nullptr;
+  a.Bp_shared = pk ? pk->gu_s : nullptr;
   a.N_routed = c.F;
   a.N_shared = c.F_shared;
   a.K_routed = c.d;
   a.K_shared = c.d;
   a.C_routed = p.H;
   a.C_shared = p.Hs;
-  hipLaunchKernelGGL(grouped_gemm_stream<true>, dim3(num_cus()), dim3(NTHREADS), 0, s, a);
-  return hipGetLastError();
+  return launch_stream(p, a, true, pk != nullptr, s);
 }
 
-hipError_t launch_stream_down(const Plan &p, const void *W2, const void *W2s, hipStream_t s) {
+hipError_t launch_stream_down(const Plan &p, const void *W2, const void *W2s, const PackedView *pk,
+                              hipStream_t s) {
   const moe_cfg &c = p.cfg;
   StreamArgs a = base_args(p, 1);
   a.A_routed = p.H;
@@ -461,14 +646,15 @@ hipError_t launch_stream_down(const Plan &p, const void *W2, const void *W2s, hi
   a.B1_routed = nullptr;
   a.B0_shared = W2s;
   a.B1_shared = nullptr;
+  a.Bp_routed = pk ? pk->dn : nullptr;
+  a.Bp_shared = pk ? pk->dn_s : nullptr;
   a.N_routed = c.d;
   a.N_shared = c.d;
   a.K_routed = c.F;
   a.K_shared = c.F_shared;
   a.C_routed = p.O;
   a.C_shared = p.Z;
-  hipLaunchKernelGGL(grouped_gemm_stream<false>, dim3(num_cus()), dim3(NTHREADS), 0, s, a);
-  return hipGetLastError();
+  return launch_stream(p, a, false, pk != nullptr, s);
 }
 
 }  // namespace moe

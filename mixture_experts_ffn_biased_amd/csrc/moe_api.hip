@@ -35,25 +35,36 @@ moe_status validate(const moe_cfg *c) {
 
 static size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// The streaming kernels need bf16, 256-row tiles with whole 128-column
-// gate/up slabs and 256-column down slabs, and enough rows per expert for a
-// 256-row tile to pay off; everything else takes the tiled kernels.
+// The streaming kernels need bf16 and whole 256-row weight slabs
+// (d % 256, F % 128, F_shared % 128).  With at least 64 routed rows per
+// expert on average they run 256-row tiles (prefill); with fewer, 32-row
+// tiles with a deeper weight ring (decode), which also needs F % 256 and
+// F_shared % 256.  Everything else takes the tiled kernels.
 static int choose_path(const moe_cfg &c) {
   if (c.dtype != MOE_BF16) return PATH_TILED;
   if (c.d % 256 != 0 || c.F % 128 != 0 || c.F_shared % 128 != 0) return PATH_TILED;
   const int64_t S = c.T * c.k;
-  if (S < 64LL * c.E) return PATH_TILED;
-  const int64_t m = stream_tile_m();
+  int path = PATH_STREAM;
+  if (S < 64LL * c.E) {
+    if (c.F % 256 != 0 || c.F_shared % 256 != 0) return PATH_TILED;
+    path = PATH_STREAM_DECODE;
+  }
+  const int64_t m = stream_tile_m(path);
   const int64_t chunks = S / (2 * m) + c.E + c.T / (2 * m) + 4;
   if (chunks > stream_max_chunks()) return PATH_TILED;
-  return PATH_STREAM;
+  return path;
+}
+
+// Packed weights serve every T: both streaming variants read them.
+static bool packable(const moe_cfg &c) {
+  return c.dtype == MOE_BF16 && c.d % 256 == 0 && c.F % 256 == 0 && c.F_shared % 256 == 0;
 }
 
 void make_plan(const moe_cfg &c, void *base, Plan *p) {
   p->cfg = c;
   p->S = c.T * c.k;
   p->path = choose_path(c);
-  p->tile_m = p->path == PATH_STREAM ? stream_tile_m() : gemm_tile_m(c.dtype);
+  p->tile_m = p->path == PATH_TILED ? gemm_tile_m(c.dtype) : stream_tile_m(p->path);
   p->n_perm_blocks = (p->S + kPermChunk - 1) / kPermChunk;
   p->max_tiles = (p->S + p->tile_m - 1) / p->tile_m + c.E +
                  (c.F_shared > 0 ? (c.T + p->tile_m - 1) / p->tile_m : 0);
@@ -74,7 +85,7 @@ void make_plan(const moe_cfg &c, void *base, Plan *p) {
   p->tiles = static_cast<Tile *>(take(sizeof(Tile) * p->max_tiles));
   p->tile_count = static_cast<int32_t *>(take(sizeof(int32_t)));
   p->max_items_gu = p->max_items_dn = 0;
-  if (p->path == PATH_STREAM) {
+  if (p->path != PATH_TILED) {
     const int64_t nslab = stream_nslab_gate_up(c.F > c.F_shared ? c.F : c.F_shared);
     p->max_items_gu = p->max_tiles * nslab;
     p->max_items_dn = p->max_tiles * stream_nslab_down(c.d);
@@ -152,6 +163,74 @@ static moe_status prepare(const moe_cfg *cfg, void *workspace, size_t workspace_
   return MOE_OK;
 }
 
+// Validation shared by the two forward entry points; *p is filled on success.
+static moe_status check_forward(const void *u, const void *W_router, const moe_cfg *cfg, const void *y,
+                                const int32_t *topk_idx, const float *gates, void *workspace,
+                                size_t workspace_bytes, Plan *p) {
+  if (!u || !W_router || !y || !topk_idx || !gates) return MOE_ERR_NULL;
+  if (!aligned16(u) || !aligned16(W_router) || !aligned16(y)) return MOE_ERR_ALIGN;
+  const size_t bytes = static_cast<size_t>(cfg->T) * cfg->d * (cfg->dtype == MOE_BF16 ? 2 : 4);
+  const char *a = static_cast<const char *>(u);
+  const char *b = static_cast<const char *>(y);
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_SHAPE;  // y aliases u
+  return prepare(cfg, workspace, workspace_bytes, p);
+}
+
+static moe_status run_layer(const Plan &p, const void *u, const void *W_router, const float *bias,
+                            const void *W1, const void *W3, const void *W2, const moe_shared *shared,
+                            const PackedView *pk, void *y, int32_t *topk_idx, float *gates,
+                            hipStream_t s) {
+  (void)hipGetLastError();  // report only errors of the launches below
+  Record rec{};
+  bool timed = false;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_timing && g_records.size() < kMaxRecords) {
+      int made = 0;
+      for (auto &e : rec.ev) {
+        if (hipEventCreate(&e) != hipSuccess) break;
+        ++made;
+      }
+      if (made != MOE_N_STAGES + 1) {
+        for (int i = 0; i < made; ++i) (void)hipEventDestroy(rec.ev[i]);
+        return MOE_ERR_HIP;
+      }
+      timed = true;
+    }
+  }
+  auto mark = [&](int i) {
+    if (timed) (void)hipEventRecord(rec.ev[i], s);
+  };
+  auto fail = [&]() {
+    if (timed) {
+      (void)hipStreamSynchronize(s);
+      for (auto &e : rec.ev) (void)hipEventDestroy(e);
+    }
+    return MOE_ERR_HIP;
+  };
+  const void *W1s = shared ? shared->W1 : nullptr, *W3s = shared ? shared->W3 : nullptr;
+  const void *W2s = shared ? shared->W2 : nullptr;
+  mark(0);
+  if (launch_router_topk(p, u, W_router, bias, topk_idx, gates, s) != hipSuccess) return fail();
+  mark(1);
+  if (launch_permute(p, topk_idx, s) != hipSuccess) return fail();
+  mark(2);
+  hipError_t err = p.path == PATH_TILED ? launch_gate_up(p, u, W1, W3, W1s, W3s, s)
+                                        : launch_stream_gate_up(p, u, W1, W3, W1s, W3s, pk, s);
+  if (err != hipSuccess) return fail();
+  mark(3);
+  err = p.path == PATH_TILED ? launch_down(p, W2, W2s, s) : launch_stream_down(p, W2, W2s, pk, s);
+  if (err != hipSuccess) return fail();
+  mark(4);
+  if (launch_combine(p, gates, y, s) != hipSuccess) return fail();
+  mark(5);
+  if (timed) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_records.push_back(rec);
+  }
+  return MOE_OK;
+}
+
 moe_status moe_layer_forward(const void *u, const void *W_router, const float *bias, const void *W1,
                              const void *W3, const void *W2, const moe_shared *shared,
                              const moe_cfg *cfg, void *y, int32_t *topk_idx, float *gates,
@@ -160,60 +239,64 @@ moe_status moe_layer_forward(const void *u, const void *W_router, const float *b
   if (st != MOE_OK) return st;
   if ((cfg->F_shared > 0) != (shared != nullptr)) return MOE_ERR_CFG;
   if (cfg->T == 0) return MOE_OK;
-  if (!u || !W_router || !W1 || !W3 || !W2 || !y || !topk_idx || !gates) return MOE_ERR_NULL;
+  if (!W1 || !W3 || !W2) return MOE_ERR_NULL;
   if (shared && (!shared->W1 || !shared->W3 || !shared->W2)) return MOE_ERR_NULL;
-  const void *ptrs[] = {u, W_router, W1, W3, W2, y, shared ? shared->W1 : u,
-                        shared ? shared->W3 : u, shared ? shared->W2 : u};
+  const void *ptrs[] = {W1, W3, W2, shared ? shared->W1 : W1, shared ? shared->W3 : W1,
+                        shared ? shared->W2 : W1};
   for (const void *q : ptrs)
     if (!aligned16(q)) return MOE_ERR_ALIGN;
-  {
-    const size_t bytes = static_cast<size_t>(cfg->T) * cfg->d * (cfg->dtype == MOE_BF16 ? 2 : 4);
-    const char *a = static_cast<const char *>(u);
-    const char *b = static_cast<const char *>(y);
-    if (a < b + bytes && b < a + bytes) return MOE_ERR_SHAPE;  // y aliases u
-  }
   Plan p;
-  st = prepare(cfg, workspace, workspace_bytes, &p);
+  st = check_forward(u, W_router, cfg, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
+  return run_layer(p, u, W_router, bias, W1, W3, W2, shared, nullptr, y, topk_idx, gates,
+                   static_cast<hipStream_t>(stream));
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();  // report only errors of the launches below
+size_t moe_packed_weights_bytes(const moe_cfg *cfg) {
+  if (validate(cfg) != MOE_OK || !packable(*cfg)) return 0;
+  return packed_weights_bytes(*cfg);
+}
 
-  Record rec{};
-  bool timed = false;
-  {
-    std::lock_guard<std::mutex> lk(g_mu);
-    if (g_timing && g_records.size() < kMaxRecords) {
-      timed = true;
-      for (auto &e : rec.ev)
-        if (hipEventCreate(&e) != hipSuccess) return MOE_ERR_HIP;
-    }
-  }
-  auto mark = [&](int i) {
-    if (timed) (void)hipEventRecord(rec.ev[i], s);
-  };
-
-  mark(0);
-  if (launch_router_topk(p, u, W_router, bias, topk_idx, gates, s) != hipSuccess) return MOE_ERR_HIP;
-  mark(1);
-  if (launch_permute(p, topk_idx, s) != hipSuccess) return MOE_ERR_HIP;
-  mark(2);
-  const void *W1s = shared ? shared->W1 : nullptr, *W3s = shared ? shared->W3 : nullptr;
-  const void *W2s = shared ? shared->W2 : nullptr;
-  hipError_t err = p.path == PATH_STREAM ? launch_stream_gate_up(p, u, W1, W3, W1s, W3s, s)
-                                         : launch_gate_up(p, u, W1, W3, W1s, W3s, s);
-  if (err != hipSuccess) return MOE_ERR_HIP;
-  mark(3);
-  err = p.path == PATH_STREAM ? launch_stream_down(p, W2, W2s, s) : launch_down(p, W2, W2s, s);
-  if (err != hipSuccess) return MOE_ERR_HIP;
-  mark(4);
-  if (launch_combine(p, gates, y, s) != hipSuccess) return MOE_ERR_HIP;
-  mark(5);
-  if (timed) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    g_records.push_back(rec);
-  }
+moe_status moe_pack_weights(const moe_cfg *cfg, const void *W1, const void *W3, const void *W2,
+                            const moe_shared *shared, void *packed, size_t packed_bytes, void *stream) {
+  moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if (!packable(*cfg)) return MOE_ERR_SHAPE;
+  if ((cfg->F_shared > 0) != (shared != nullptr)) return MOE_ERR_CFG;
+  if (!W1 || !W3 || !W2 || !packed) return MOE_ERR_NULL;
+  if (shared && (!shared->W1 || !shared->W3 || !shared->W2)) return MOE_ERR_NULL;
+  if (packed_bytes < packed_weights_bytes(*cfg)) return MOE_ERR_WORKSPACE;
+  const void *ptrs[] = {W1, W3, W2, packed, shared ? shared->W1 : W1, shared ? shared->W3 : W1,
+                        shared ? shared->W2 : W1};
+  for (const void *q : ptrs)
+    if (!aligned16(q)) return MOE_ERR_ALIGN;
+  (void)hipGetLastError();
+  if (launch_pack_weights(*cfg, W1, W3, W2, shared ? shared->W1 : nullptr, shared ? shared->W3 : nullptr,
+                          shared ? shared->W2 : nullptr, packed, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+moe_status moe_layer_forward_packed(const void *u, const void *W_router, const float *bias,
+                                    const void *packed, const moe_cfg *cfg, void *y, int32_t *topk_idx,
+                                    float *gates, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if (!packable(*cfg)) return MOE_ERR_SHAPE;
+  if (cfg->T == 0) return MOE_OK;
+  if (!packed) return MOE_ERR_NULL;
+  if (!aligned16(packed)) return MOE_ERR_ALIGN;
+  Plan p;
+  st = check_forward(u, W_router, cfg, y, topk_idx, gates, workspace, workspace_bytes, &p);
+  if (st != MOE_OK) return st;
+  if (p.path == PATH_TILED) return MOE_ERR_SHAPE;  // too many tiles for the streaming schedule
+  const PackedView pk = packed_view(*cfg, packed);
+  // The shared expert is present iff F_shared > 0; its pointers come from pk.
+  moe_shared sh{pk.gu_s, pk.gu_s, pk.dn_s};
+  return run_layer(p, u, W_router, bias, nullptr, nullptr, nullptr, cfg->F_shared > 0 ? &sh : nullptr,
+                   &pk, y, topk_idx, gates, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_route_debug(const void *u, const void *W_router, const float *bias, const moe_cfg *cfg,

@@ -127,7 +127,7 @@ hipError_t launch_permute(const Plan &p, const int32_t *topk_idx, hipStream_t s)
                      p.tiles, p.tile_count);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (p.path == PATH_STREAM) {
+  if (p.path != PATH_TILED) {
     err = launch_stream_schedule(p, s);
     if (err != hipSuccess) return err;
   }

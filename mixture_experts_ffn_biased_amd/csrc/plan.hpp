@@ -27,8 +27,17 @@ constexpr int kMaxGroups = 64;
 
 // Which grouped-GEMM kernels run the experts.
 enum GemmPath {
-  PATH_TILED = 0,   // grouped_gemm.hip: 128-row tiles (fp32 too), any size multiple of 64
-  PATH_STREAM = 1,  // gemm_stream.hip: persistent, 256-row tiles, bf16 prefill shapes
+  PATH_TILED = 0,          // grouped_gemm.hip: 128-row tiles (fp32 too), any size multiple of 64
+  PATH_STREAM = 1,         // gemm_stream.hip prefill variant: 256-row tiles
+  PATH_STREAM_DECODE = 2,  // gemm_stream.hip decode variant: 32-row tiles, deep weight ring
+};
+
+// Device views of the four regions of a packed weight buffer.
+struct PackedView {
+  const void *gu;    // routed W1/W3 stage blocks
+  const void *dn;    // routed W2
+  const void *gu_s;  // shared W1/W3
+  const void *dn_s;  // shared W2
 };
 
 struct Plan {
@@ -70,13 +79,20 @@ hipError_t launch_gate_up(const Plan &p, const void *u, const void *W1, const vo
 hipError_t launch_down(const Plan &p, const void *W2, const void *W2s, hipStream_t s);
 hipError_t launch_combine(const Plan &p, const float *gates, void *y, hipStream_t s);
 
-int stream_tile_m();
+int stream_tile_m(int path);
 int stream_max_chunks();
 int stream_nslab_gate_up(int F);
 int stream_nslab_down(int d);
+size_t packed_weights_bytes(const moe_cfg &c);
+PackedView packed_view(const moe_cfg &c, const void *base);
+hipError_t launch_pack_weights(const moe_cfg &c, const void *W1, const void *W3, const void *W2,
+                               const void *W1s, const void *W3s, const void *W2s, void *packed,
+                               hipStream_t s);
 hipError_t launch_stream_schedule(const Plan &p, hipStream_t s);
+// pk == nullptr: plain weight layout; else the packed buffer's regions.
 hipError_t launch_stream_gate_up(const Plan &p, const void *u, const void *W1, const void *W3,
-                                 const void *W1s, const void *W3s, hipStream_t s);
-hipError_t launch_stream_down(const Plan &p, const void *W2, const void *W2s, hipStream_t s);
+                                 const void *W1s, const void *W3s, const PackedView *pk, hipStream_t s);
+hipError_t launch_stream_down(const Plan &p, const void *W2, const void *W2s, const PackedView *pk,
+                              hipStream_t s);
 
 }  // namespace moe

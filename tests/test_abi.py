@@ -90,8 +90,19 @@ def test_gemm_path_selection():
     assert path["tiny_fp32"] == "tiled"
     assert path["dsv3_prefill"] == "stream" and path["mixtral_e8_top2"] == "stream"
     assert path["skewed_e128_top8"] == "stream"
+    assert path["dsv3_decode"] == "stream_decode"
     assert moe.moe_plan_describe(cfg(d=192))[0] == "tiled"
     assert moe.moe_plan_describe(cfg(T=8, n_groups=1, topk_groups=1))[0] == "tiled"
+
+
+def test_packed_weight_size_is_the_weight_bytes():
+    for name in ("mixtral_e8_top2", "dsv3_prefill", "dsv3_decode", "skewed_e128_top8"):
+        w = WORKLOADS[name]
+        c = moe.MoeConfig.from_workload(w)
+        want = 2 * (3 * w.E * w.F * w.d + 3 * w.Fs * w.d)
+        assert moe.moe_packed_weights_bytes(c) == want
+    assert moe.moe_packed_weights_bytes(moe.MoeConfig.from_workload(WORKLOADS["tiny_fp32"])) == 0
+    assert moe.moe_packed_weights_bytes(cfg(d=256, F=384)) == 0  # F not a multiple of 256
 
 
 def _call(c, **ptrs):

@@ -17,7 +17,7 @@ import oracle
 from oracle import balance, skew
 from parity import (Y_TOL, host, mode_of, oracle_inputs, rel_l2, route_parity, sampled_outputs,
                     widen_gpu)
-from synthetic import WORKLOADS, Workload, make_inputs
+from synthetic import WORKLOADS, Workload, make_inputs, make_u
 
 pytestmark = pytest.mark.gpu
 
@@ -112,10 +112,19 @@ STREAM = {
 }
 
 
-@pytest.mark.parametrize("name", list(STREAM))
+DECODE = {
+    "decode_sigmoid_groups_shared": Workload("decode_sigmoid_groups_shared", 40, 256, 16, 4, 256, 256,
+                                             "sigmoid", 4, 2, 2.5, "bf16", "uniform"),
+    "decode_softmax_e64": Workload("decode_softmax_e64", 37, 512, 64, 6, 512, 0, "softmax", 1, 1,
+                                   1.0, "bf16", "uniform"),
+}
+
+
+@pytest.mark.parametrize("name", list(STREAM) + list(DECODE))
 def test_stream_path_every_token(dev, name):
-    w = STREAM[name]
-    assert moe.moe_plan_describe(moe.MoeConfig.from_workload(w))[0] == "stream"
+    w = STREAM.get(name) or DECODE[name]
+    assert moe.moe_plan_describe(moe.MoeConfig.from_workload(w))[0] == (
+        "stream" if name in STREAM else "stream_decode")
     log(f"[stream] {name}")
     inp = to_dev(make_inputs(w, seed=7, device="cpu"), dev)
     y, idx, g = run(w, inp)
@@ -133,6 +142,35 @@ def test_stream_path_one_expert_takes_every_token(dev):
     y, idx, g = run(w, inp)
     assert (idx[:, 0] == 0).all()
     check_full(w, inp, y, idx, g)
+
+
+PACKABLE = {
+    "stream_softmax": STREAM["stream_softmax"],
+    "decode_sigmoid_groups_shared": DECODE["decode_sigmoid_groups_shared"],
+    "prefill_sigmoid_groups_shared": Workload("prefill_sigmoid_groups_shared", 900, 512, 16, 4, 256, 512,
+                                              "sigmoid", 4, 2, 2.5, "bf16", "uniform"),
+}
+
+
+def run_packed(w, inp, packed):
+    cfg = moe.MoeConfig.from_workload(w)
+    out = moe.moe_layer_forward_packed(inp["u"], inp["W_router"], inp["bias"], packed, cfg=cfg)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name", list(PACKABLE))
+def test_packed_weights_give_bitwise_identical_layer(dev, name):
+    """The packed layout changes where weights live, not the arithmetic."""
+    w = PACKABLE[name]
+    inp = to_dev(make_inputs(w, seed=9, device="cpu"), dev)
+    cfg = moe.MoeConfig.from_workload(w)
+    packed = moe.moe_pack_weights(inp["W1"], inp["W3"], inp["W2"], inp["shared"], cfg=cfg)
+    ref = run(w, inp)
+    got = run_packed(w, inp, packed)
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    check_full(w, inp, *got)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -254,6 +292,25 @@ def test_mixtral_full_size(dev):
     inp = make_inputs(w, seed=0, device=dev)
     check_large(w, inp, n_sample=24)
     del inp
+
+
+def test_dsv3_prefill_and_decode_full_size_packed(dev):
+    """Packed-weight forward at the DSv3 prefill and decode shapes (the
+    benchmark's launch configuration) is bitwise the plain forward, which
+    the two tests below check against the oracle."""
+    w = WORKLOADS["dsv3_prefill"]
+    inp = make_inputs(w, seed=0, device=dev)
+    cfg = moe.MoeConfig.from_workload(w)
+    packed = moe.moe_pack_weights(inp["W1"], inp["W3"], inp["W2"], inp["shared"], cfg=cfg)
+    for wl in (w, WORKLOADS["dsv3_decode"]):
+        u = inp["u"] if wl.T == w.T else make_u(wl, seed=0, device=dev)
+        x = dict(inp, u=u)
+        ref = run(wl, x)
+        got = run_packed(wl, x, packed)
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), wl.name
+        log(f"[packed] {wl.name} bitwise equal to the plain-weight forward")
+    del inp, packed
 
 
 def test_dsv3_prefill_full_size(dev):
