@@ -8,6 +8,10 @@ expert width 2048, bf16 with fp32 accumulation): router + top-k, permutation,
 gate/up + SiLU*mul, down, combine.  Inputs are seeded synthetic tensors,
 resident in HBM before the timed region starts.
 
+The expert weights are packed once before timing (moe_pack_weights: a
+one-time re-layout done at model load, identical results); the plain-layout
+timing is reported beside it.
+
 Printed: one JSON line with tokens/s, the layer's TFLOP/s and fraction of the
 bf16 MFMA peak, the roofline of the dominant kernel (gate/up, from HIP events
 recorded by the library on the launch stream during the timed steps), the
@@ -44,6 +48,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="tokens whose expert outputs the CPU oracle computes")
+    ap.add_argument("--plain-weights", action="store_true",
+                    help="time the plain weight layout instead of the packed one")
+    ap.add_argument("--no-plain", action="store_true",
+                    help="skip the reference timing of the plain weight layout")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB three times (a plain "
                          "copy kernel of known size, to scale hardware byte counters)")
@@ -55,8 +63,11 @@ def log(*a):
 
 
 def kernel_source_hash():
-    p = os.path.join(ROOT, "mixture_experts_ffn_biased_amd", "csrc", "grouped_gemm.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the sources of the streaming GEMM kernels (the dominant ones)."""
+    h = hashlib.sha256()
+    for f in ("gemm_stream.hip", "pipeline.hpp", "common.hpp", "plan.hpp"):
+        h.update(open(os.path.join(ROOT, "mixture_experts_ffn_biased_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(name):
@@ -93,7 +104,8 @@ def timed_steps(step, steps, warmup, torch):
     return ms, wall, [s / max(calls, 1) for s in stage_ms], calls
 
 
-def run_layer(w, inp, u, steps, warmup, torch):
+def run_layer(w, inp, u, steps, warmup, torch, packed=None):
+    """Time `steps` layer calls (plain weights, or the packed buffer if given)."""
     import mixture_experts_ffn_biased_amd as moe
     cfg = moe.MoeConfig.from_workload(w)
     dev = u.device
@@ -103,9 +115,13 @@ def run_layer(w, inp, u, steps, warmup, torch):
     ws = moe.alloc_workspace(cfg, dev)
 
     def step():
-        moe.moe_layer_forward(u, inp["W_router"], inp["bias"], inp["W1"], inp["W3"], inp["W2"],
-                              inp["shared"], cfg=cfg, y=y, topk_idx=idx, gates=gates,
-                              workspace=ws)
+        if packed is not None:
+            moe.moe_layer_forward_packed(u, inp["W_router"], inp["bias"], packed, cfg=cfg, y=y,
+                                         topk_idx=idx, gates=gates, workspace=ws)
+        else:
+            moe.moe_layer_forward(u, inp["W_router"], inp["bias"], inp["W1"], inp["W3"], inp["W2"],
+                                  inp["shared"], cfg=cfg, y=y, topk_idx=idx, gates=gates,
+                                  workspace=ws)
 
     ms, wall, stage_ms, calls = timed_steps(step, steps, warmup, torch)
     return ms, wall, stage_ms, idx
@@ -175,8 +191,14 @@ def main():
     inp = make_inputs(w, seed=args.seed, device=dev)
     torch.cuda.synchronize()
 
+    cfg = moe.MoeConfig.from_workload(w)
+    packed = None
+    if not args.plain_weights:
+        log("[bench] packing the expert weights (one-time layout change, not timed)")
+        packed = moe.moe_pack_weights(inp["W1"], inp["W3"], inp["W2"], inp["shared"], cfg=cfg)
+        torch.cuda.synchronize()
     log(f"[bench] {w.name}: {args.warmup} warm-up + {args.steps} timed steps")
-    ms, wall, stage_ms, idx = run_layer(w, inp, inp["u"], args.steps, args.warmup, torch)
+    ms, wall, stage_ms, idx = run_layer(w, inp, inp["u"], args.steps, args.warmup, torch, packed)
     tokens_per_s = w.T / (ms * 1e-3)
     layer_tflops = w.flops / (ms * 1e-3) / 1e12
     S = w.T * w.k
@@ -199,11 +221,12 @@ def main():
         "data": "synthetic (seeded; u ~ N(0,1), weights ~ N(0, 1/fan_in), bias ~ U(-0.05, 0.05))",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F,
                    "F_shared": w.Fs, "score_fn": w.score_fn, "n_groups": w.n_groups,
-                   "topk_groups": w.topk_groups, "route_scale": w.route_scale},
+                   "topk_groups": w.topk_groups, "route_scale": w.route_scale,
+                   "weights": "plain" if packed is None else "packed"},
         "layer_tflops": round(layer_tflops, 2),
         "layer_mfma_frac": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
         "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, stage_ms)},
-        "roofline": {"kernel": "grouped_gemm_bf16<gate_up>", "bound": "mfma",
+        "roofline": {"kernel": "gemm_stream_prefill<gate_up>", "bound": "mfma",
                      "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
@@ -213,7 +236,7 @@ def main():
         wd = WORKLOADS[args.decode_workload]
         ud = make_u(wd, seed=args.seed, device=dev)
         log(f"[bench] {wd.name}: {args.warmup} warm-up + {args.decode_steps} timed steps")
-        dms, _, dstage, didx = run_layer(wd, inp, ud, args.decode_steps, args.warmup, torch)
+        dms, _, dstage, didx = run_layer(wd, inp, ud, args.decode_steps, args.warmup, torch, packed)
         hit = int(torch.unique(didx).numel())
         s = 2
         gu_bytes = (hit * 2 * wd.F * wd.d + 2 * wd.Fs * wd.d) * s + wd.T * wd.d * s + \
@@ -228,11 +251,18 @@ def main():
             "layer_bytes": layer_bytes, "layer_GBps": round(gbs, 1),
             "layer_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
             "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, dstage)},
-            "roofline": {"kernel": "grouped_gemm_bf16<gate_up>", "bound": "hbm",
+            "roofline": {"kernel": "gemm_stream_decode<gate_up>", "bound": "hbm",
                          "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
                          "traffic": stored_traffic(f"gate_up_{wd.name}")},
         }
+
+    if packed is not None and not args.no_plain:
+        # the same layer with the weights in their plain layout, for reference
+        pms, _, pstage, _ = run_layer(w, inp, inp["u"], max(3, args.steps // 2), 2, torch, None)
+        result["plain_weights"] = {"ms_per_step": round(pms, 4),
+                                   "tokens_per_s": round(w.T / (pms * 1e-3), 1),
+                                   "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, pstage)}}
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20

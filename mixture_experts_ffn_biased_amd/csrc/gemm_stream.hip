@@ -20,7 +20,7 @@
 //    multiplied; no VGPR staging.
 //  * Prefill variant: 256-row tiles, 8 waves in a 2x4 grid (two per SIMD, one
 //    from each row half), each 128 x 64 of v_mfma_f32_32x32x16_bf16 with fp32
-//    accumulators, a 4-slot ring (96 KB in flight).  A wave multiplies only
+//    accumulators, a 4-slot ring (3 stages, 96 KB, in flight).  A wave multiplies only
 //    the 32-row blocks that hold rows of the tile (its K loop is specialised
 //    on that count), so a SIMD's MFMA work follows the tile's row count.
 //  * Decode variant (few rows per expert): 32-row tiles, 4 waves each 32 x 64,
@@ -81,55 +81,70 @@ struct Ring {
   unsigned char *s[NS];
 };
 
-template <int VAR>
+// DMA source pointers of one thread (scalar members, not arrays, so that
+// no private array is ever demoted to memory).
 struct Ptrs {
-  const uint16_t *a[V<VAR>::A_LOADS];
-  const uint16_t *b[V<VAR>::B_LOADS];
-};
-
-// Wait for stage S of the last ring turn, barrier, multiply; then the next.
-template <int NS, int PS, int S>
-struct Tail {
-  template <class C>
-  __device__ __forceinline__ static void run(const Ring<NS> &ring, C &compute) {
-    wait_vmcnt<(NS - 1 - S) * PS>();
-    raw_barrier();
-    compute(ring.s[S]);
-    Tail<NS, PS, S + 1>::run(ring, compute);
+  const uint16_t *a0, *a1;
+  const uint16_t *b0, *b1, *b2, *b3;
+  __device__ __forceinline__ const uint16_t *a(int i) const { return i == 0 ? a0 : a1; }
+  __device__ __forceinline__ const uint16_t *b(int i) const {
+    return i == 0 ? b0 : (i == 1 ? b1 : (i == 2 ? b2 : b3));
+  }
+  __device__ __forceinline__ void set_a(int i, const uint16_t *v) {
+    if (i == 0) a0 = v; else a1 = v;
+  }
+  __device__ __forceinline__ void set_b(int i, const uint16_t *v) {
+    if (i == 0) b0 = v; else if (i == 1) b1 = v; else if (i == 2) b2 = v; else b3 = v;
   }
 };
-template <int NS, int PS>
-struct Tail<NS, PS, NS> {
-  template <class C>
-  __device__ __forceinline__ static void run(const Ring<NS> &, C &) {}
+
+// The last R stages of an item (R in [NS-1, 2NS-2]), all slot indices
+// static: iteration i consumes slot i % NS, refills while stages remain, and
+// waits until at most the later stages already issued are outstanding.
+template <int NS, int PS, int R, int I>
+struct Rem {
+  template <class Issue, class Compute>
+  __device__ __forceinline__ static void run(const Ring<NS> &ring, int base, Issue &issue, Compute &compute) {
+    constexpr int LATER = (NS - 2) < (R - 1 - I) ? (NS - 2) : (R - 1 - I);
+    wait_vmcnt<LATER * PS>();
+    raw_barrier();
+    if (I < R - NS + 1) issue(ring.s[(I + NS - 1) % NS], base + I + NS - 1);
+    compute(ring.s[I % NS]);
+    Rem<NS, PS, R, I + 1>::run(ring, base, issue, compute);
+  }
+};
+template <int NS, int PS, int R>
+struct Rem<NS, PS, R, R> {
+  template <class Issue, class Compute>
+  __device__ __forceinline__ static void run(const Ring<NS> &, int, Issue &, Compute &) {}
 };
 
 // The K loop of one item for a wave with NMI active 32-row blocks.  Every
 // wave issues the same loads and barriers whatever its NMI, so waves with
 // different row counts stay in step.
 template <bool PACKED, int VAR, int NMI>
-__device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Ptrs<VAR> &p, int KT,
+__device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Ptrs &p, int KT,
                                       int wave, int lane, int wm, int wn, int fo0, int fo1,
                                       f32x16 (&acc)[4][2]) {
   constexpr int NS = V<VAR>::NSTAGE;
   constexpr int PS = V<VAR>::A_LOADS + V<VAR>::B_LOADS;  // loads per wave per stage
   constexpr int AB = a_bytes<VAR>();
-  auto issue = [&](unsigned char *st, int kt) {
+  auto issue = [&](unsigned char *st, int kt) __attribute__((always_inline)) {
     const int koff = kt * SBK;
     if (VAR == 0) {
 #pragma unroll
-      for (int i = 0; i < V<VAR>::A_LOADS; ++i) dma16(p.a[i] + koff, st + (wave * 2 + i) * 1024);
+      for (int i = 0; i < V<VAR>::A_LOADS; ++i) dma16(p.a(i) + koff, st + (wave * 2 + i) * 1024);
     } else {
       // 32 rows: each wave loads 8 rows with its first 32 lanes.
-      if (lane < 32) dma16(p.a[0] + koff, st + wave * 512);
+      if (lane < 32) dma16(p.a(0) + koff, st + wave * 512);
     }
 #pragma unroll
     for (int i = 0; i < V<VAR>::B_LOADS; ++i) {
-      const uint16_t *src = PACKED ? p.b[i] + static_cast<int64_t>(kt) * B_STAGE_ELEMS : p.b[i] + koff;
+      const uint16_t *src = PACKED ? p.b(i) + static_cast<int64_t>(kt) * B_STAGE_ELEMS : p.b(i) + koff;
       dma16(src, st + AB + (wave * V<VAR>::B_LOADS + i) * 1024);
     }
   };
-  auto compute = [&](const unsigned char *st) {
+  auto compute = [&](const unsigned char *st) __attribute__((always_inline)) {
     if (NMI == 0) return;
     const unsigned char *sa = st + wm * 128 * 64;
     const unsigned char *sb = st + AB + wn * 64 * 64;
@@ -150,10 +165,12 @@ __device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Pt
   };
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) issue(ring.s[i], i);
-  // Stage kt lives in slot kt % NS (unrolled: static slot indices).  It is
-  // complete once at most the NS-2 later stages are outstanding; after the
-  // barrier, stage kt+NS-1 refills the slot of stage kt-1.
-  for (int j = 0; j < KT / NS - 1; ++j) {
+  // Stage kt lives in slot kt % NS (unrolled by NS: static slot indices).  It
+  // is complete once at most the NS-2 later stages are outstanding; after
+  // the barrier, stage kt+NS-1 refills the slot of stage kt-1.  G full turns
+  // of the ring issue a stage every iteration; the last R stages follow.
+  const int G = (KT - NS + 1) / NS;
+  for (int j = 0; j < G; ++j) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       wait_vmcnt<(NS - 2) * PS>();
@@ -162,11 +179,8 @@ __device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Pt
       compute(ring.s[s]);
     }
   }
-  wait_vmcnt<(NS - 2) * PS>();
-  raw_barrier();
-  issue(ring.s[NS - 1], KT - 1);
-  compute(ring.s[0]);
-  Tail<NS, PS, 1>::run(ring, compute);
+  // K is a multiple of NS stages (the plan guarantees it), so R == NS.
+  Rem<NS, PS, NS, 0>::run(ring, G * NS, issue, compute);
 }
 
 template <bool DUAL, bool PACKED, int VAR>
@@ -195,12 +209,12 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   // DMA sources.  A load fills 16 LDS rows (8 in the decode variant, first
   // 32 lanes); lane l lands in row +l/4, physical chunk l%4, which holds
   // logical k-chunk (l%4) ^ ((row>>2)&3).
-  Ptrs<VAR> p;
+  Ptrs p{};
 #pragma unroll
   for (int i = 0; i < V<VAR>::A_LOADS; ++i) {
     const int r = VAR == 0 ? (wave * 2 + i) * 16 + (lane >> 2) : wave * 8 + ((lane & 31) >> 2);
     const int c = (lane & 3) ^ ((r >> 2) & 3);
-    p.a[i] = a_row(r) + c * 8;
+    p.set_a(i, a_row(r) + c * 8);
   }
   if (PACKED) {
     // The slab's stage blocks are contiguous: block kt at kt * B_STAGE_ELEMS,
@@ -210,7 +224,7 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
     const int64_t slab = (shared ? 0 : static_cast<int64_t>(tl.group) * nslab) + item.y;
     const uint16_t *blk = Bp + slab * KT * B_STAGE_ELEMS;
 #pragma unroll
-    for (int i = 0; i < V<VAR>::B_LOADS; ++i) p.b[i] = blk + (wave * V<VAR>::B_LOADS + i) * 512 + lane * 8;
+    for (int i = 0; i < V<VAR>::B_LOADS; ++i) p.set_b(i, blk + (wave * V<VAR>::B_LOADS + i) * 512 + lane * 8);
   } else {
     const uint16_t *B0 = static_cast<const uint16_t *>(shared ? g.B0_shared : g.B0_routed);
     const uint16_t *B1 = static_cast<const uint16_t *>(shared ? g.B1_shared : g.B1_routed);
@@ -233,7 +247,7 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
       } else {
         brow = n0 + r;
       }
-      p.b[i] = bsrc + brow * K + c * 8;
+      p.set_b(i, bsrc + brow * K + c * 8);
     }
   }
 
@@ -330,9 +344,11 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   }
 }
 
+// The ring is idle between items, so the fetched item index is broadcast
+// through the first word of slot 0.
 template <bool DUAL, bool PACKED, int VAR>
-__device__ __forceinline__ void item_loop(const StreamArgs &g, const Ring<V<VAR>::NSTAGE> &ring,
-                                          int *item_sh) {
+__device__ __forceinline__ void item_loop(const StreamArgs &g, const Ring<V<VAR>::NSTAGE> &ring) {
+  int *item_sh = reinterpret_cast<int *>(ring.s[0]);
   const int xcd = blockIdx.x & 7;
   for (int o = 0; o < 8; ++o) {
     const int x = (xcd + o) & 7;
@@ -355,13 +371,12 @@ template <bool DUAL, bool PACKED>
 __global__ __launch_bounds__(512, 1) void gemm_stream_prefill(StreamArgs g) {
   constexpr int SB = stage_bytes<0>();
   __shared__ __attribute__((aligned(16))) unsigned char r0[SB], r1[SB], r2[SB], r3[SB];
-  __shared__ int item_sh;
   Ring<4> ring;
   ring.s[0] = r0;
   ring.s[1] = r1;
   ring.s[2] = r2;
   ring.s[3] = r3;
-  item_loop<DUAL, PACKED, 0>(g, ring, &item_sh);
+  item_loop<DUAL, PACKED, 0>(g, ring);
 }
 
 template <bool DUAL, bool PACKED>
@@ -369,7 +384,6 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_decode(StreamArgs g) {
   constexpr int SB = stage_bytes<1>();
   __shared__ __attribute__((aligned(16))) unsigned char r0[SB], r1[SB], r2[SB], r3[SB], r4[SB], r5[SB],
       r6[SB], r7[SB];
-  __shared__ int item_sh;
   Ring<8> ring;
   ring.s[0] = r0;
   ring.s[1] = r1;
@@ -379,7 +393,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_decode(StreamArgs g) {
   ring.s[5] = r5;
   ring.s[6] = r6;
   ring.s[7] = r7;
-  item_loop<DUAL, PACKED, 1>(g, ring, &item_sh);
+  item_loop<DUAL, PACKED, 1>(g, ring);
 }
 
 // ---- one-time weight packing -------------------------------------------------

@@ -65,6 +65,7 @@ void make_plan(const moe_cfg &c, void *base, Plan *p) {
   p->S = c.T * c.k;
   p->path = choose_path(c);
   p->tile_m = p->path == PATH_TILED ? gemm_tile_m(c.dtype) : stream_tile_m(p->path);
+  p->router_splits = (c.dtype == MOE_BF16 && c.d % 128 == 0) ? router_splits(c.T, c.d) : 1;
   p->n_perm_blocks = (p->S + kPermChunk - 1) / kPermChunk;
   p->max_tiles = (p->S + p->tile_m - 1) / p->tile_m + c.E +
                  (c.F_shared > 0 ? (c.T + p->tile_m - 1) / p->tile_m : 0);
@@ -76,6 +77,8 @@ void make_plan(const moe_cfg &c, void *base, Plan *p) {
     off += align_up(bytes);
     return ptr;
   };
+  p->router_part = static_cast<float *>(
+      take(p->router_splits > 1 ? sizeof(float) * p->router_splits * c.T * c.E : 0));
   p->blk_counts = static_cast<int32_t *>(take(sizeof(int32_t) * p->n_perm_blocks * c.E));
   p->blk_base = static_cast<int32_t *>(take(sizeof(int32_t) * p->n_perm_blocks * c.E));
   p->counts = static_cast<int32_t *>(take(sizeof(int32_t) * c.E));

@@ -45,6 +45,8 @@ struct Plan {
   int path;         // GemmPath
   int64_t S;        // routed slots, T*k
   int tile_m;       // rows per grouped-GEMM tile
+  int router_splits;    // K splits of the router GEMM (1 = fused with selection)
+  float *router_part;   // [router_splits][T][E] partial logits when router_splits > 1
   int64_t n_perm_blocks;
   int64_t max_tiles;
   // workspace carve-up (device pointers; null when only sizing)
@@ -68,6 +70,7 @@ struct Plan {
 };
 
 moe_status validate(const moe_cfg *c);
+int router_splits(int64_t T, int d);
 // Fills *p; base == nullptr computes only the size.
 void make_plan(const moe_cfg &c, void *base, Plan *p);
 

@@ -374,12 +374,187 @@ __global__ __launch_bounds__(256, 1) void router_topk_stream(
   }
 }
 
+// ---- split-K router for bf16, d % 128 == 0 ------------------------------------
+//
+// When few 64-token tiles exist (decode) or the K loop is long, the router
+// GEMM is split over K: workgroup (m, s) computes the partial logits of 64
+// tokens over K range s and stores them (fp32); router_select then adds the
+// splits in a fixed order (deterministic) and selects.
+
+template <int NB>
+__global__ __launch_bounds__(256, 2) void router_logits_split(
+    const uint16_t *__restrict__ u, const uint16_t *__restrict__ Wr, int64_t T, int d, int E,
+    int kt_per_split, float *__restrict__ part) {
+  constexpr int A_B = kRowsS * 64;
+  constexpr int B_B = NB * 64 * 64;
+  constexpr int SLOT = A_B + B_B;
+  constexpr int PER_STAGE = 1 + NB;
+  __shared__ __attribute__((aligned(16))) unsigned char ring0[SLOT];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[SLOT];
+  __shared__ __attribute__((aligned(16))) unsigned char ring2[SLOT];
+  __shared__ __attribute__((aligned(16))) unsigned char ring3[SLOT];
+  unsigned char *const ring[4] = {ring0, ring1, ring2, ring3};
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRowsS;
+  const int split = blockIdx.y;
+  const int k_begin = split * kt_per_split * 32;
+
+  const int sub = lane >> 2;
+  const uint16_t *ap;
+  {
+    const int r = wave * 16 + sub;
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    int64_t t = t0 + r;
+    if (t >= T) t = T - 1;
+    ap = u + t * d + k_begin + c * 8;
+  }
+  const uint16_t *bp[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int r = (wave * NB + j) * 16 + sub;
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int e = r < E ? r : E - 1;
+    bp[j] = Wr + static_cast<int64_t>(e) * d + k_begin + c * 8;
+  }
+  auto issue = [&](unsigned char *st, int kt) {
+    const int koff = kt * 32;
+    dma16(ap + koff, st + wave * 1024);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) dma16(bp[j] + koff, st + A_B + (wave * NB + j) * 1024);
+  };
+  const int sw = (lane >> 2) & 3;
+  const int fo0 = (lane & 31) * 64 + (((0 + (lane >> 5)) ^ sw) << 4);
+  const int fo1 = (lane & 31) * 64 + (((2 + (lane >> 5)) ^ sw) << 4);
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+  const int wcol = wave < NB ? wave : 0;
+  auto compute = [&](const unsigned char *st) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int fo = kk ? fo1 : fo0;
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) a[mi] = *reinterpret_cast<const bf16x8 *>(st + mi * 2048 + fo);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        b[ni] = *reinterpret_cast<const bf16x8 *>(st + A_B + (wcol * 64 + ni * 32) * 64 + fo);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+  };
+  const int KT = kt_per_split;  // multiple of 4, >= 4
+  issue(ring[0], 0);
+  issue(ring[1], 1);
+  issue(ring[2], 2);
+  for (int j = 0; j < KT / 4 - 1; ++j) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      wait_vmcnt<2 * PER_STAGE>();
+      raw_barrier();
+      issue(ring[(s4 + 3) & 3], j * 4 + s4 + 3);
+      compute(ring[s4]);
+    }
+  }
+  wait_vmcnt<2 * PER_STAGE>();
+  raw_barrier();
+  issue(ring[3], KT - 1);
+  compute(ring[0]);
+  wait_vmcnt<2 * PER_STAGE>();
+  raw_barrier();
+  compute(ring[1]);
+  wait_vmcnt<PER_STAGE>();
+  raw_barrier();
+  compute(ring[2]);
+  wait_vmcnt<0>();
+  raw_barrier();
+  compute(ring[3]);
+
+  if (wave < NB) {
+    float *out = part + (static_cast<int64_t>(split) * T) * E;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = wave * 64 + ni * 32 + (lane & 31);
+          const int64_t t = t0 + row;
+          if (col < E && t < T) out[t * E + col] = acc[mi][ni][r];
+        }
+  }
+}
+
+// One wave per token: logits = sum of the splits in order, then selection.
+__global__ __launch_bounds__(256) void router_select(const float *__restrict__ part, int nsplit,
+                                                     int64_t T, SelArgs sel,
+                                                     int32_t *__restrict__ topk_idx,
+                                                     float *__restrict__ gates) {
+  __shared__ float lg[4][kLogitStride];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int E = sel.E;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * 16 + wave; t < T && t < (blockIdx.x + 1) * 16LL;
+       t += 4) {
+    for (int e = lane; e < E; e += 64) {
+      // four independent partial sums (splits sp % 4), added in a fixed order
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      int sp = 0;
+      for (; sp + 4 <= nsplit; sp += 4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += part[(static_cast<int64_t>(sp + i) * T + t) * E + e];
+      for (int i = 0; sp + i < nsplit; ++i) v[i] += part[(static_cast<int64_t>(sp + i) * T + t) * E + e];
+      lg[wave][e] = (v[0] + v[1]) + (v[2] + v[3]);
+    }
+    select_token(lg[wave], sel, topk_idx + t * sel.k, gates + t * sel.k);
+  }
+}
+
 }  // namespace
+
+int router_splits(int64_t T, int d) {
+  // Split K so that about 2 workgroups per CU (512) run, each >= 4 stages.
+  const int64_t mt = (T + kRowsS - 1) / kRowsS;
+  const int q = d / 128;  // stage groups of 4
+  int best = 1;
+  for (int s = 1; s <= q && s <= 16; ++s)
+    if (q % s == 0 && mt * s <= 512) best = s;
+  return best;
+}
 
 hipError_t launch_router_topk(const Plan &p, const void *u, const void *Wr, const float *bias,
                               int32_t *topk_idx, float *gates, hipStream_t s) {
   const moe_cfg &c = p.cfg;
   SelArgs sel{c.E, c.k, c.score_fn, c.n_groups, c.topk_groups, c.route_scale, bias};
+  if (c.dtype == MOE_BF16 && c.d % 128 == 0 && p.router_splits > 1) {
+    const int S = p.router_splits;
+    const dim3 grid(static_cast<unsigned>((c.T + kRowsS - 1) / kRowsS), static_cast<unsigned>(S));
+    const int ktps = c.d / 32 / S;
+    auto *U = static_cast<const uint16_t *>(u);
+    auto *W = static_cast<const uint16_t *>(Wr);
+    const int nb = (c.E + 63) / 64;
+    if (nb == 1)
+      hipLaunchKernelGGL(router_logits_split<1>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part);
+    else if (nb == 2)
+      hipLaunchKernelGGL(router_logits_split<2>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part);
+    else if (nb == 3)
+      hipLaunchKernelGGL(router_logits_split<3>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part);
+    else
+      hipLaunchKernelGGL(router_logits_split<4>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(router_select, dim3(static_cast<unsigned>((c.T + 15) / 16)), dim3(256), 0, s,
+                       p.router_part, S, c.T, sel, topk_idx, gates);
+    return hipGetLastError();
+  }
   if (c.dtype == MOE_BF16 && c.d % 128 == 0) {
     const dim3 grid(static_cast<unsigned>((c.T + kRowsS - 1) / kRowsS));
     const int nb = (c.E + 63) / 64;
