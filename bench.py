@@ -82,6 +82,38 @@ def stored_traffic(name):
     return rec.get("hbm_bytes_per_launch")
 
 
+def roofline(kernel, flops, nbytes, ms, traffic):
+    """Roofline of one kernel from its algorithmic FLOPs and bytes per launch
+    and its average launch time: the bound is whichever peak gives the
+    longer lower-bound time; both fractions are reported."""
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    s = ms * 1e-3
+    tflops = flops / s / 1e12
+    gbs = nbytes / s / 1e9
+    out = {"kernel": kernel}
+    if t_hbm >= t_mfma:
+        out.update(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                   frac=round(gbs / PEAK_HBM_GBS, 4))
+    else:
+        out.update(bound="mfma", achieved=round(tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                   frac=round(tflops / PEAK_BF16_TFLOPS, 4))
+    out.update(traffic=traffic, ms=round(ms, 4), alg_flops=flops, alg_bytes=int(nbytes),
+               mfma_frac=round(tflops / PEAK_BF16_TFLOPS, 4), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
+               ridge_flop_per_byte=round(PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9), 1),
+               flop_per_byte=round(flops / nbytes, 1))
+    return out
+
+
+def gate_up_bytes(w, hit, s=2):
+    """Algorithmic HBM bytes of one gate/up launch: the W1 and W3 rows of every
+    expert hit and of the shared expert once, each routed slot's token row
+    gathered once and its F-wide activation written once, the same per token
+    for the shared expert."""
+    return ((hit * 2 * w.F * w.d + 2 * w.Fs * w.d) * s + (w.T * w.k + (w.T if w.Fs else 0)) * w.d * s
+            + (w.T * w.k * w.F + w.T * w.Fs) * s)
+
+
 def timed_steps(step, steps, warmup, torch):
     import mixture_experts_ffn_biased_amd as moe
     for _ in range(warmup):
@@ -203,9 +235,7 @@ def main():
     layer_tflops = w.flops / (ms * 1e-3) / 1e12
     S = w.T * w.k
     gu_flops = 4.0 * w.d * (w.F * S + w.Fs * w.T)
-    gu_ms = stage_ms[GATE_UP]
-    gu_tflops = gu_flops / (gu_ms * 1e-3) / 1e12
-    traffic = stored_traffic(f"gate_up_{w.name}")
+    hit_p = int(torch.unique(idx).numel())
     result = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -226,10 +256,9 @@ def main():
         "layer_tflops": round(layer_tflops, 2),
         "layer_mfma_frac": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
         "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, stage_ms)},
-        "roofline": {"kernel": "gemm_stream_prefill<gate_up>", "bound": "mfma",
-                     "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic},
+        "experts_hit": hit_p,
+        "roofline": roofline("gemm_stream_prefill<gate_up>", gu_flops, gate_up_bytes(w, hit_p),
+                             stage_ms[GATE_UP], stored_traffic(f"gate_up_{w.name}")),
     }
 
     if not args.no_decode:
@@ -239,22 +268,18 @@ def main():
         dms, _, dstage, didx = run_layer(wd, inp, ud, args.decode_steps, args.warmup, torch, packed)
         hit = int(torch.unique(didx).numel())
         s = 2
-        gu_bytes = (hit * 2 * wd.F * wd.d + 2 * wd.Fs * wd.d) * s + wd.T * wd.d * s + \
-            (wd.T * wd.k * wd.F + wd.T * wd.Fs) * s
         layer_bytes = (wd.E * wd.d * s + 4 * wd.E + hit * 3 * wd.d * wd.F * s + 3 * wd.d * wd.Fs * s
                        + 2 * wd.T * wd.d * s + 8 * wd.T * wd.k)
         gbs = layer_bytes / (dms * 1e-3) / 1e9
-        gu_gbs = gu_bytes / (dstage[GATE_UP] * 1e-3) / 1e9
+        gu_flops_d = 4.0 * wd.d * (wd.F * wd.T * wd.k + wd.Fs * wd.T)
         result["decode"] = {
             "workload": wd.name, "T": wd.T, "ms_per_step": round(dms, 4),
             "tokens_per_s": round(wd.T / (dms * 1e-3), 1), "experts_hit": hit,
             "layer_bytes": layer_bytes, "layer_GBps": round(gbs, 1),
             "layer_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
             "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, dstage)},
-            "roofline": {"kernel": "gemm_stream_decode<gate_up>", "bound": "hbm",
-                         "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
-                         "traffic": stored_traffic(f"gate_up_{wd.name}")},
+            "roofline": roofline("gemm_stream_decode<gate_up>", gu_flops_d, gate_up_bytes(wd, hit),
+                                 dstage[GATE_UP], stored_traffic(f"gate_up_{wd.name}")),
         }
 
     if packed is not None and not args.no_plain:
