@@ -564,6 +564,10 @@ StreamArgs base_args(const Plan &p, int list) {
 }  // namespace
 
 int stream_tile_m(int path) { return path == PATH_STREAM_DECODE ? V<1>::BM : V<0>::BM; }
+// Prefill tiles of one expert get equal row counts (same tile count), so the
+// two tiles of a chunk, which share its weight slabs, run for the same time
+// and read each slab together.
+int stream_tile_balanced(int path) { return path == PATH_STREAM ? 1 : 0; }
 int stream_max_chunks() { return kMaxChunks; }
 int stream_nslab_gate_up(int F) { return F / (SBN / 2); }
 int stream_nslab_down(int d) { return d / SBN; }

@@ -65,6 +65,7 @@ void make_plan(const moe_cfg &c, void *base, Plan *p) {
   p->S = c.T * c.k;
   p->path = choose_path(c);
   p->tile_m = p->path == PATH_TILED ? gemm_tile_m(c.dtype) : stream_tile_m(p->path);
+  p->tile_balanced = p->path == PATH_TILED ? 0 : stream_tile_balanced(p->path);
   p->router_splits = (c.dtype == MOE_BF16 && c.d % 128 == 0) ? router_splits(c.T, c.d) : 1;
   p->n_perm_blocks = (p->S + kPermChunk - 1) / kPermChunk;
   p->max_tiles = (p->S + p->tile_m - 1) / p->tile_m + c.E +

@@ -46,7 +46,7 @@ __device__ int exclusive_scan_256(int v, int *buf, int *total) {
 // One block: totals per expert, offsets, per-block bases, and the GEMM tiles.
 __global__ __launch_bounds__(256) void perm_scan(
     const int32_t *__restrict__ blk_counts, int nblk, int E, int64_t S, int64_t T, int has_shared,
-    int tile_m, int32_t *__restrict__ blk_base, int32_t *__restrict__ counts,
+    int tile_m, int balanced, int32_t *__restrict__ blk_base, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, Tile *__restrict__ tiles, int32_t *__restrict__ tile_count) {
   __shared__ int buf[256];
   const int e = threadIdx.x;
@@ -66,8 +66,10 @@ __global__ __launch_bounds__(256) void perm_scan(
       run += blk_counts[static_cast<int64_t>(b) * E + e];
     }
     for (int i = 0; i < nt; ++i) {
-      const int r0 = i * tile_m;
-      tiles[toff + i] = Tile{e, off + r0, c - r0 < tile_m ? c - r0 : tile_m, 0};
+      int64_t r0;
+      int n;
+      tile_rows(c, nt, i, tile_m, balanced, &r0, &n);
+      tiles[toff + i] = Tile{e, off + static_cast<int32_t>(r0), n, 0};
     }
   }
   if (e == 0) offsets[E] = static_cast<int32_t>(S);
@@ -75,9 +77,10 @@ __global__ __launch_bounds__(256) void perm_scan(
   if (has_shared) {
     ns = static_cast<int>((T + tile_m - 1) / tile_m);
     for (int i = e; i < ns; i += 256) {
-      const int64_t r0 = static_cast<int64_t>(i) * tile_m;
-      tiles[total_tiles + i] =
-          Tile{E, static_cast<int32_t>(r0), static_cast<int32_t>(T - r0 < tile_m ? T - r0 : tile_m), 0};
+      int64_t r0;
+      int n;
+      tile_rows(T, ns, i, tile_m, balanced, &r0, &n);
+      tiles[total_tiles + i] = Tile{E, static_cast<int32_t>(r0), n, 0};
     }
   }
   if (e == 0) *tile_count = total_tiles + ns;
@@ -123,7 +126,7 @@ hipError_t launch_permute(const Plan &p, const int32_t *topk_idx, hipStream_t s)
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(perm_scan, dim3(1), dim3(256), 0, s, p.blk_counts, static_cast<int>(nblk), c.E,
-                     p.S, c.T, c.F_shared > 0 ? 1 : 0, p.tile_m, p.blk_base, p.counts, p.offsets,
+                     p.S, c.T, c.F_shared > 0 ? 1 : 0, p.tile_m, p.tile_balanced, p.blk_base, p.counts, p.offsets,
                      p.tiles, p.tile_count);
   err = hipGetLastError();
   if (err != hipSuccess) return err;

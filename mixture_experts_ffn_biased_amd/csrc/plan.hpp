@@ -20,6 +20,22 @@ struct Tile {
   int32_t pad;
 };
 
+// Row range of tile i of the nt = ceil(c / tile_m) tiles over c rows.
+// balanced 0: tiles of tile_m rows, the last one ragged; balanced 1: the rows
+// spread evenly (sizes differ by at most one), so tiles that share weight
+// slabs carry the same work.
+__host__ __device__ inline void tile_rows(int64_t c, int nt, int i, int tile_m, int balanced, int64_t *r0,
+                                          int *n) {
+  if (!balanced) {
+    *r0 = static_cast<int64_t>(i) * tile_m;
+    *n = static_cast<int>(c - *r0 < tile_m ? c - *r0 : tile_m);
+  } else {
+    const int64_t base = c / nt, rem = c % nt;
+    *r0 = i * base + (i < rem ? i : rem);
+    *n = static_cast<int>(base + (i < rem ? 1 : 0));
+  }
+}
+
 constexpr int kPermChunk = 1024;  // slots per block in the permutation kernels
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 32;
@@ -44,7 +60,8 @@ struct Plan {
   moe_cfg cfg;
   int path;         // GemmPath
   int64_t S;        // routed slots, T*k
-  int tile_m;       // rows per grouped-GEMM tile
+  int tile_m;       // rows per grouped-GEMM tile (at most)
+  int tile_balanced;  // tile_rows rule
   int router_splits;    // K splits of the router GEMM (1 = fused with selection)
   float *router_part;   // [router_splits][T][E] partial logits when router_splits > 1
   int64_t n_perm_blocks;
@@ -84,6 +101,7 @@ hipError_t launch_combine(const Plan &p, const float *gates, void *y, hipStream_
 
 int stream_tile_m(int path);
 int stream_max_chunks();
+int stream_tile_balanced(int path);
 int stream_nslab_gate_up(int F);
 int stream_nslab_down(int d);
 size_t packed_weights_bytes(const moe_cfg &c);
