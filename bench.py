@@ -261,6 +261,22 @@ def main():
                              stage_ms[GATE_UP], stored_traffic(f"gate_up_{w.name}")),
     }
 
+    # one aux-loss-free balance step on this layer's routing (bias updated on a copy)
+    bias_copy = inp["bias"].clone()
+    for _ in range(5):
+        moe.moe_balance_update(idx, bias_copy, E=w.E)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(100):
+        moe.moe_balance_update(idx, bias_copy, E=w.E)
+    e1.record()
+    torch.cuda.synchronize()
+    bu_ms = e0.elapsed_time(e1) / 100
+    bu_bytes = 4 * w.T * w.k + 12 * w.E
+    result["balance_update"] = {"us": round(bu_ms * 1e3, 2), "slots": w.T * w.k,
+                                "GBps": round(bu_bytes / (bu_ms * 1e-3) / 1e9, 1)}
+
     if not args.no_decode:
         wd = WORKLOADS[args.decode_workload]
         ud = make_u(wd, seed=args.seed, device=dev)

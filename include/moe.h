@@ -164,6 +164,28 @@ moe_status moe_route_debug(const void *u, const void *W_router, const float *bia
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * One step of the auxiliary-loss-free balance update ("Mixture of Experts and
+ * Hybrid Architectures", "Aux-loss-free balance loop"; the bias moves only
+ * selection, "Sparse MoE FFN", "How it works", Routing), from the routing of
+ * one batch:
+ *   counts[e] = number of the T*k entries of topk_idx equal to e
+ *   target    = T*k / E
+ *   bias[e]  -= gamma  if counts[e] > target   (compared exactly: counts*E vs T*k)
+ *   bias[e]  += gamma  if counts[e] < target   (fp32 add; an expert on target keeps its bias)
+ *   *entropy  = -sum_e p_e ln p_e, p = counts / (T*k) (0 when T == 0; max ln E)
+ *   topk_idx [T][k] int32   device, as written by moe_layer_forward; entries
+ *                           outside [0, E) are not counted; may be NULL if T == 0
+ *   bias     [E]    fp32    device, updated in place
+ *   counts   [E]    int32   device out, may be NULL
+ *   entropy  [1]    fp32    device out, may be NULL (computed in fp64)
+ * Enqueued on stream as one kernel; allocates nothing and needs no workspace.
+ * Returns MOE_ERR_SHAPE for T < 0, k outside 1..32 or E outside 1..256,
+ * MOE_ERR_CFG for a non-finite gamma, MOE_ERR_NULL, MOE_ERR_ALIGN (4 bytes).
+ */
+moe_status moe_balance_update(const int32_t *topk_idx, int64_t T, int32_t k, int32_t E, float gamma,
+                              float *bias, int32_t *counts, float *entropy, void *stream);
+
+/*
  * Which grouped-GEMM kernels moe_layer_forward uses for cfg (host only, no
  * GPU call): *gemm_path = 0 for the tiled kernels (any size, fp32 or bf16),
  * 1 for the persistent weight-streaming kernels with 256-row tiles (bf16,

@@ -101,6 +101,8 @@ def lib():
         L.moe_layer_forward.restype = I32
         L.moe_route_debug.argtypes = [P, P, P, CP, P, P, P, P, P, P, P, SZ, P]
         L.moe_route_debug.restype = I32
+        L.moe_balance_update.argtypes = [P, I64, I32, I32, ctypes.c_float, P, P, P, P]
+        L.moe_balance_update.restype = I32
         L.moe_packed_weights_bytes.argtypes = [CP]
         L.moe_packed_weights_bytes.restype = SZ
         L.moe_pack_weights.argtypes = [CP, P, P, P, ctypes.POINTER(moe_shared), P, SZ, P]
@@ -311,6 +313,28 @@ def moe_route_debug(u, W_router, bias, *, cfg: MoeConfig, workspace=None, stream
     if st != 0:
         raise MoeError(st, "moe_route_debug")
     return topk_idx, gates, counts, offsets, perm, inv
+
+
+def moe_balance_update(topk_idx, bias, *, E: int, gamma: float = 0.15, counts=None, entropy=None,
+                       stream=None):
+    """One aux-loss-free balance step on the routing topk_idx [T][k] (int32):
+    updates bias [E] (fp32) in place; returns (counts [E] int32, entropy [1] fp32)."""
+    dev = bias.device
+    _need(bias, (E,), torch.float32, "bias", dev)
+    if topk_idx.dim() != 2 or topk_idx.dtype != torch.int32 or topk_idx.device != dev:
+        raise ValueError("topk_idx must be an int32 [T][k] tensor on the bias device")
+    if not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be contiguous")
+    T, k = topk_idx.shape
+    if counts is None:
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+    if entropy is None:
+        entropy = torch.empty(1, dtype=torch.float32, device=dev)
+    st = lib().moe_balance_update(_ptr(topk_idx) if T > 0 else None, T, k, E, float(gamma), _ptr(bias),
+                                  _ptr(counts), _ptr(entropy), _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_balance_update")
+    return counts, entropy
 
 
 def moe_timing_enable(on: bool) -> None:

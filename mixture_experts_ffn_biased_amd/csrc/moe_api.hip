@@ -11,6 +11,9 @@
 namespace moe {
 
 int gemm_tile_m(int dtype);
+// balance.hip
+hipError_t launch_balance_update(const int32_t *topk_idx, int64_t S, int E, float gamma, float *bias,
+                                 int32_t *counts, float *entropy, hipStream_t s);
 
 moe_status validate(const moe_cfg *c) {
   if (!c) return MOE_ERR_NULL;
@@ -301,6 +304,21 @@ moe_status moe_layer_forward_packed(const void *u, const void *W_router, const f
   moe_shared sh{pk.gu_s, pk.gu_s, pk.dn_s};
   return run_layer(p, u, W_router, bias, nullptr, nullptr, nullptr, cfg->F_shared > 0 ? &sh : nullptr,
                    &pk, y, topk_idx, gates, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_balance_update(const int32_t *topk_idx, int64_t T, int32_t k, int32_t E, float gamma,
+                              float *bias, int32_t *counts, float *entropy, void *stream) {
+  if (T < 0 || k < 1 || k > kMaxTopK || E < 1 || E > kMaxExperts) return MOE_ERR_SHAPE;
+  if (T * static_cast<int64_t>(k) > 0x7fffffffLL - 1024) return MOE_ERR_SHAPE;
+  if (!std::isfinite(gamma)) return MOE_ERR_CFG;
+  if (!bias || (T > 0 && !topk_idx)) return MOE_ERR_NULL;
+  auto al4 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 3u) == 0; };
+  if (!al4(bias) || !al4(topk_idx) || !al4(counts) || !al4(entropy)) return MOE_ERR_ALIGN;
+  (void)hipGetLastError();
+  if (launch_balance_update(topk_idx, T * k, E, gamma, bias, counts, entropy, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 moe_status moe_route_debug(const void *u, const void *W_router, const float *bias, const moe_cfg *cfg,

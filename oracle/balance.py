@@ -42,6 +42,33 @@ def update_bias(bias, counts, target, gamma=0.15):
     return b
 
 
+def update_step_fp32(idx, E, bias32, gamma32):
+    """One balance step in the precision a GPU keeps the bias in.
+
+    idx: the routing of one batch (any shape); entries outside [0, E) are not
+    counted but still count in S = idx.size, the number of (token, slot)
+    pairs.  target = S / E; the comparisons are made exactly, as count * E
+    against S.  The bias update is done in fp64 on the fp32 bias and gamma
+    (exact for values of this size) and rounded once to fp32.  The entropy is
+    -sum p ln p with p = count / S (0 when S == 0).
+
+    Returns (new bias fp32 [E], counts int64 [E], entropy fp64)."""
+    flat = np.asarray(idx).reshape(-1)
+    S = flat.size
+    counts = np.bincount(flat[(flat >= 0) & (flat < E)].astype(np.int64), minlength=E)
+    ce = counts * E
+    b = np.asarray(bias32, dtype=np.float32).astype(np.float64)
+    g = float(np.float32(gamma32))
+    b[ce > S] -= g
+    b[ce < S] += g
+    if S > 0:
+        p = counts[counts > 0] / S
+        ent = float(-(p * np.log(p)).sum())
+    else:
+        ent = 0.0
+    return b.astype(np.float32), counts, ent
+
+
 def balance_bias(logits, k, gamma=0.15, iterations=10, score_fn=SOFTMAX, n_groups=1,
                  topk_groups=1, nthreads=None):
     """Run the loop on fixed logits [T][E].

@@ -143,3 +143,17 @@ def test_seeded_inputs_are_deterministic():
     assert x["W1"].dtype == torch.bfloat16 and x["bias"].abs().max() <= 0.05
     std = x["W1"].float().std().item()
     assert abs(std - 1 / 8) < 0.02  # 1/sqrt(d)
+
+
+def test_balance_update_arguments_are_checked_before_any_launch():
+    L = moe.lib()
+    f = ctypes.c_void_p
+    idx, bias, cnt, ent = f(0x10000), f(0x20000), f(0x30000), f(0x40000)
+    call = lambda T=8, k=2, E=16, g=0.15, i=idx, b=bias, c=cnt, e=ent: L.moe_balance_update(
+        i, T, k, E, ctypes.c_float(g), b, c, e, None)
+    assert call(T=-1) == -2
+    assert call(k=0) == -2 and call(k=33) == -2
+    assert call(E=0) == -2 and call(E=257) == -2
+    assert call(g=float("nan")) == -3 and call(g=float("inf")) == -3
+    assert call(b=None) == -1 and call(i=None) == -1
+    assert call(b=f(0x20002)) == -7 and call(c=f(0x30001)) == -7

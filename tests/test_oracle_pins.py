@@ -358,3 +358,34 @@ def test_invalid_configurations_are_rejected():
     for k, G, M in ((9, 1, 1), (2, 3, 1), (2, 8, 4), (5, 4, 2)):
         with pytest.raises(ValueError):
             oracle.select(lg, k, oracle.SIGMOID, G, M)
+
+
+def test_balance_step_hand_worked():
+    """One step of the balance update ("Mixture of Experts and Hybrid
+    Architectures", "Aux-loss-free balance loop") on a routing small enough to
+    follow by hand: 3 tokens, k = 2, E = 4, picks (0,1), (0,2), (0,1).
+    counts = [3, 2, 1, 0], S = 6, target = 6/4 = 1.5: experts 0 and 1 are over
+    (bias - gamma), 2 and 3 under (+ gamma); p = [1/2, 1/3, 1/6, 0], entropy =
+    (1/2) ln 2 + (1/3) ln 3 + (1/6) ln 6."""
+    g = np.float32(0.15)
+    b, c, h = balance.update_step_fp32(np.array([[0, 1], [0, 2], [0, 1]]), 4,
+                                       np.array([0.5, 0, 0, -1], np.float32), g)
+    assert c.tolist() == [3, 2, 1, 0]
+    assert b.tolist() == [np.float32(0.5) - g, -g, g, np.float32(-1) + g]
+    assert h == pytest.approx(0.5 * math.log(2) + math.log(3) / 3 + math.log(6) / 6, rel=1e-15)
+    # on target exactly: E = 2, one token picking both -> counts [1, 1] = target 1, bias kept
+    b, c, h = balance.update_step_fp32(np.array([[1, 0]]), 2, np.array([0.25, -0.5], np.float32), g)
+    assert b.tolist() == [0.25, -0.5] and c.tolist() == [1, 1] and h == pytest.approx(math.log(2))
+    # entries outside [0, E) are not counted but stay in S; no tokens: nothing moves
+    b, c, h = balance.update_step_fp32(np.array([[0, 7], [-1, 0]]), 2, np.zeros(2, np.float32), g)
+    assert c.tolist() == [2, 0] and b.tolist() == [0.0, g]  # S = 4, target 2: expert 0 on target
+    assert h == pytest.approx(-0.5 * math.log(0.5))
+    b, c, h = balance.update_step_fp32(np.zeros((0, 2), np.int32), 3, np.ones(3, np.float32), g)
+    assert b.tolist() == [1, 1, 1] and c.tolist() == [0, 0, 0] and h == 0.0
+    # the fp32 step equals the fp64 loop's update rounded once
+    rng = np.random.default_rng(5)
+    idx = rng.integers(0, 16, size=(500, 4))
+    b0 = (rng.integers(-10, 10, 16) * 0.15).astype(np.float32)
+    b, c, _ = balance.update_step_fp32(idx, 16, b0, g)
+    ref = balance.update_bias(b0.astype(np.float64), balance.usage(idx, 16), 500 * 4 / 16, float(g))
+    assert np.array_equal(b, ref.astype(np.float32))
