@@ -261,6 +261,33 @@ def main():
                              stage_ms[GATE_UP], stored_traffic(f"gate_up_{w.name}")),
     }
 
+    # the layer inside its pre-norm residual block: y = u + MoE(RMSNorm(u))
+    if packed is not None:
+        from synthetic import make_norm_weight
+        g = make_norm_weight(w, seed=args.seed, device=dev)
+        bws = moe.alloc_block_workspace(cfg, dev)
+        yb = torch.empty_like(inp["u"])
+
+        def block_step():
+            moe.moe_block_forward_packed(inp["u"], g, 1e-6, inp["W_router"], inp["bias"], packed, cfg=cfg, y=yb,
+                                         workspace=bws)
+        bms, _, _, _ = timed_steps(block_step, args.steps, args.warmup, torch)
+        un = torch.empty_like(inp["u"])
+        for _ in range(5):
+            moe.moe_rmsnorm(inp["u"], g, 1e-6, out=un)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(50):
+            moe.moe_rmsnorm(inp["u"], g, 1e-6, out=un)
+        e1.record()
+        torch.cuda.synchronize()
+        nms = e0.elapsed_time(e1) / 50
+        result["block"] = {"ms_per_step": round(bms, 4), "tokens_per_s": round(w.T / (bms * 1e-3), 1),
+                           "rmsnorm_us": round(nms * 1e3, 2),
+                           "rmsnorm_GBps": round(2 * w.T * w.d * 2 / (nms * 1e-3) / 1e9, 1)}
+        del bws, yb, un
+
     # one aux-loss-free balance step on this layer's routing (bias updated on a copy)
     bias_copy = inp["bias"].clone()
     for _ in range(5):

@@ -164,6 +164,41 @@ moe_status moe_route_debug(const void *u, const void *W_router, const float *bia
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The layer inside its pre-norm residual block: y = h + MoE(RMSNorm(h)).
+ * "Lesson 2 -- From the Dense FFN to a Layer of Experts", section 2: the MoE
+ * layer takes the FFN's place in the pre-norm block, H' = H~ + MoE(Norm(H~));
+ * "Sparse MoE FFN" (DeepSeek-V3), eq. 12 and "How it works": the skip adds
+ * the block input outside the MoE module; "Mixture of experts and
+ * architecture families": the norm is RMSNorm (no mean-centering).
+ *
+ * moe_rmsnorm: out[t][j] = h[t][j] / sqrt(mean_j h[t][j]^2 + eps) * g[j],
+ *   h, out [T][d] and g [d] in dtype (device, 16-byte aligned; out may be h);
+ *   fp32 arithmetic, one rounding to dtype.  d % 64 == 0, d <= 8192,
+ *   0 <= eps finite.  T == 0 is a no-op.
+ * moe_block_workspace_bytes: workspace of the block entry points (the
+ *   layer's plus room for the normalised rows), 0 when cfg is invalid.
+ * moe_block_forward, moe_block_forward_packed: moe_layer_forward and
+ *   moe_layer_forward_packed on u = moe_rmsnorm(h, norm_weight, norm_eps)
+ *   (computed into the workspace, read by the router and the expert GEMMs),
+ *   with h added to y last in fp32 before the rounding to dtype:
+ *     y[t] = h[t] + shared(u[t]) + sum_j gates[t][j] * expert_j(u[t]).
+ *   h [T][d] and norm_weight [d] in cfg->dtype; y must not alias h;
+ *   workspace_bytes >= moe_block_workspace_bytes(cfg).  Errors as for the
+ *   layer entry points, plus MOE_ERR_CFG for a bad norm_eps.
+ */
+moe_status moe_rmsnorm(const void *h, const void *norm_weight, float eps, int64_t T, int32_t d, int32_t dtype,
+                       void *out, void *stream);
+size_t moe_block_workspace_bytes(const moe_cfg *cfg);
+moe_status moe_block_forward(const void *h, const void *norm_weight, float norm_eps, const void *W_router,
+                             const float *bias, const void *W1, const void *W3, const void *W2,
+                             const moe_shared *shared, const moe_cfg *cfg, void *y, int32_t *topk_idx,
+                             float *gates, void *workspace, size_t workspace_bytes, void *stream);
+moe_status moe_block_forward_packed(const void *h, const void *norm_weight, float norm_eps, const void *W_router,
+                                    const float *bias, const void *packed, const moe_cfg *cfg, void *y,
+                                    int32_t *topk_idx, float *gates, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/*
  * One step of the auxiliary-loss-free balance update ("Mixture of Experts and
  * Hybrid Architectures", "Aux-loss-free balance loop"; the bias moves only
  * selection, "Sparse MoE FFN", "How it works", Routing), from the routing of

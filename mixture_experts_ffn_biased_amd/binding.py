@@ -103,6 +103,16 @@ def lib():
         L.moe_route_debug.restype = I32
         L.moe_balance_update.argtypes = [P, I64, I32, I32, ctypes.c_float, P, P, P, P]
         L.moe_balance_update.restype = I32
+        F32 = ctypes.c_float
+        L.moe_rmsnorm.argtypes = [P, P, F32, I64, I32, I32, P, P]
+        L.moe_rmsnorm.restype = I32
+        L.moe_block_workspace_bytes.argtypes = [CP]
+        L.moe_block_workspace_bytes.restype = SZ
+        L.moe_block_forward.argtypes = [P, P, F32, P, P, P, P, P, ctypes.POINTER(moe_shared), CP, P, P, P,
+                                        P, SZ, P]
+        L.moe_block_forward.restype = I32
+        L.moe_block_forward_packed.argtypes = [P, P, F32, P, P, P, CP, P, P, P, P, SZ, P]
+        L.moe_block_forward_packed.restype = I32
         L.moe_packed_weights_bytes.argtypes = [CP]
         L.moe_packed_weights_bytes.restype = SZ
         L.moe_pack_weights.argtypes = [CP, P, P, P, ctypes.POINTER(moe_shared), P, SZ, P]
@@ -284,6 +294,109 @@ def moe_layer_forward_packed(u, W_router, bias, packed, *, cfg: MoeConfig, y=Non
                                         _ptr(workspace), workspace.numel(), _stream(dev, stream))
     if st != 0:
         raise MoeError(st, "moe_layer_forward_packed")
+    return y, topk_idx, gates
+
+
+def moe_rmsnorm(h, norm_weight, eps: float, *, out=None, stream=None):
+    """out = h / sqrt(mean(h^2, -1) + eps) * norm_weight, rows of h [T][d] (bf16 or fp32)."""
+    dev = h.device
+    if h.dim() != 2 or h.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("h must be a [T][d] bf16 or fp32 tensor")
+    T, d = h.shape
+    _need(h, (T, d), h.dtype, "h", dev)
+    _need(norm_weight, (d,), h.dtype, "norm_weight", dev)
+    if out is None:
+        out = torch.empty_like(h)
+    _need(out, (T, d), h.dtype, "out", dev)
+    dtype = MOE_BF16 if h.dtype == torch.bfloat16 else MOE_F32
+    st = lib().moe_rmsnorm(_ptr(h), _ptr(norm_weight), float(eps), T, d, dtype, _ptr(out), _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_rmsnorm")
+    return out
+
+
+def moe_block_workspace_bytes(cfg: MoeConfig) -> int:
+    c = cfg.to_c()
+    return int(lib().moe_block_workspace_bytes(ctypes.byref(c)))
+
+
+def alloc_block_workspace(cfg: MoeConfig, device) -> torch.Tensor:
+    n = moe_block_workspace_bytes(cfg)
+    if n == 0 and cfg.T > 0:
+        raise MoeError(moe_check_cfg(cfg) or -2, "moe_block_workspace_bytes")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _block_outputs(cfg, dev, y, topk_idx, gates):
+    dt = cfg.torch_dtype
+    T, d, k = cfg.T, cfg.d, cfg.k
+    if y is None:
+        y = torch.empty((T, d), dtype=dt, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if gates is None:
+        gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(y, (T, d), dt, "y", dev)
+    _need(topk_idx, (T, k), torch.int32, "topk_idx", dev)
+    _need(gates, (T, k), torch.float32, "gates", dev)
+    return y, topk_idx, gates
+
+
+def moe_block_forward(h, norm_weight, norm_eps, W_router, bias, W1, W3, W2, shared=None, *, cfg: MoeConfig,
+                      y=None, topk_idx=None, gates=None, workspace=None, stream=None):
+    """y = h + MoE(RMSNorm(h)); returns (y, topk_idx, gates)."""
+    dev = h.device
+    dt = cfg.torch_dtype
+    T, d, E, F, Fs = cfg.T, cfg.d, cfg.E, cfg.F, cfg.F_shared
+    _need(h, (T, d), dt, "h", dev)
+    _need(norm_weight, (d,), dt, "norm_weight", dev)
+    _need(W_router, (E, d), dt, "W_router", dev)
+    _need(W1, (E, F, d), dt, "W1", dev)
+    _need(W3, (E, F, d), dt, "W3", dev)
+    _need(W2, (E, d, F), dt, "W2", dev)
+    if bias is not None:
+        _need(bias, (E,), torch.float32, "bias", dev)
+    sh = None
+    if shared is not None:
+        W1s, W3s, W2s = shared
+        _need(W1s, (Fs, d), dt, "W1s", dev)
+        _need(W3s, (Fs, d), dt, "W3s", dev)
+        _need(W2s, (d, Fs), dt, "W2s", dev)
+        sh = moe_shared(W1s.data_ptr(), W3s.data_ptr(), W2s.data_ptr())
+    y, topk_idx, gates = _block_outputs(cfg, dev, y, topk_idx, gates)
+    if workspace is None:
+        workspace = alloc_block_workspace(cfg, dev)
+    c = cfg.to_c()
+    st = lib().moe_block_forward(_ptr(h), _ptr(norm_weight), float(norm_eps), _ptr(W_router), _ptr(bias),
+                                 _ptr(W1), _ptr(W3), _ptr(W2), ctypes.byref(sh) if sh is not None else None,
+                                 ctypes.byref(c), _ptr(y), _ptr(topk_idx), _ptr(gates), _ptr(workspace),
+                                 workspace.numel(), _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_block_forward")
+    return y, topk_idx, gates
+
+
+def moe_block_forward_packed(h, norm_weight, norm_eps, W_router, bias, packed, *, cfg: MoeConfig, y=None,
+                             topk_idx=None, gates=None, workspace=None, stream=None):
+    """moe_block_forward with weights from moe_pack_weights."""
+    dev = h.device
+    dt = cfg.torch_dtype
+    T, d, E = cfg.T, cfg.d, cfg.E
+    _need(h, (T, d), dt, "h", dev)
+    _need(norm_weight, (d,), dt, "norm_weight", dev)
+    _need(W_router, (E, d), dt, "W_router", dev)
+    if bias is not None:
+        _need(bias, (E,), torch.float32, "bias", dev)
+    _need(packed, (moe_packed_weights_bytes(cfg),), torch.uint8, "packed", dev)
+    y, topk_idx, gates = _block_outputs(cfg, dev, y, topk_idx, gates)
+    if workspace is None:
+        workspace = alloc_block_workspace(cfg, dev)
+    c = cfg.to_c()
+    st = lib().moe_block_forward_packed(_ptr(h), _ptr(norm_weight), float(norm_eps), _ptr(W_router),
+                                        _ptr(bias), _ptr(packed), ctypes.byref(c), _ptr(y), _ptr(topk_idx),
+                                        _ptr(gates), _ptr(workspace), workspace.numel(), _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_block_forward_packed")
     return y, topk_idx, gates
 
 

@@ -17,7 +17,8 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
                                                     const uint16_t *__restrict__ Z,
                                                     const int32_t *__restrict__ inv,
                                                     const float *__restrict__ gates, int64_t T,
-                                                    int d, int k, uint16_t *__restrict__ y) {
+                                                    int d, int k, const uint16_t *__restrict__ R,
+                                                    uint16_t *__restrict__ y) {
   const int64_t t = blockIdx.x;
   const int nchunk = d / 8;
   __shared__ int pos[kMaxTopK];
@@ -51,6 +52,15 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
         acc[2 * i + 1] = fmaf(g, bf16_to_f32(static_cast<uint16_t>(w[i] >> 16)), acc[2 * i + 1]);
       }
     }
+    if (R) {  // the block's residual, added last
+      const uint4 r = *reinterpret_cast<const uint4 *>(R + t * d + c * 8);
+      const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(rw[i] & 0xffffu));
+        acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(rw[i] >> 16));
+      }
+    }
     uint4 out;
     out.x = pack_bf16x2(acc[0], acc[1]);
     out.y = pack_bf16x2(acc[2], acc[3]);
@@ -64,7 +74,7 @@ __global__ __launch_bounds__(256) void combine_f32(const float *__restrict__ O,
                                                    const float *__restrict__ Z,
                                                    const int32_t *__restrict__ inv,
                                                    const float *__restrict__ gates, int64_t T, int d,
-                                                   int k, float *__restrict__ y) {
+                                                   int k, const float *__restrict__ R, float *__restrict__ y) {
   const int64_t t = blockIdx.x;
   __shared__ int pos[kMaxTopK];
   __shared__ float gw[kMaxTopK];
@@ -83,24 +93,31 @@ __global__ __launch_bounds__(256) void combine_f32(const float *__restrict__ O,
       acc.z = fmaf(g, o.z, acc.z);
       acc.w = fmaf(g, o.w, acc.w);
     }
+    if (R) {  // the block's residual, added last
+      const float4 r = *reinterpret_cast<const float4 *>(R + t * d + c * 4);
+      acc.x += r.x;
+      acc.y += r.y;
+      acc.z += r.z;
+      acc.w += r.w;
+    }
     *reinterpret_cast<float4 *>(y + t * d + c * 4) = acc;
   }
 }
 
 }  // namespace
 
-hipError_t launch_combine(const Plan &p, const float *gates, void *y, hipStream_t s) {
+hipError_t launch_combine(const Plan &p, const float *gates, const void *residual, void *y, hipStream_t s) {
   const moe_cfg &c = p.cfg;
   const void *Z = c.F_shared > 0 ? p.Z : nullptr;
   const dim3 grid(static_cast<unsigned>(c.T));
   if (c.dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_bf16, grid, dim3(256), 0, s, static_cast<const uint16_t *>(p.O),
                        static_cast<const uint16_t *>(Z), p.inv, gates, c.T, c.d, c.k,
-                       static_cast<uint16_t *>(y));
+                       static_cast<const uint16_t *>(residual), static_cast<uint16_t *>(y));
   else
     hipLaunchKernelGGL(combine_f32, grid, dim3(256), 0, s, static_cast<const float *>(p.O),
                        static_cast<const float *>(Z), p.inv, gates, c.T, c.d, c.k,
-                       static_cast<float *>(y));
+                       static_cast<const float *>(residual), static_cast<float *>(y));
   return hipGetLastError();
 }
 

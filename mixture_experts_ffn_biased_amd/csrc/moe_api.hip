@@ -183,10 +183,11 @@ static moe_status check_forward(const void *u, const void *W_router, const moe_c
   return prepare(cfg, workspace, workspace_bytes, p);
 }
 
+// residual: nullptr for the layer, the block input h for the block form.
 static moe_status run_layer(const Plan &p, const void *u, const void *W_router, const float *bias,
                             const void *W1, const void *W3, const void *W2, const moe_shared *shared,
                             const PackedView *pk, void *y, int32_t *topk_idx, float *gates,
-                            hipStream_t s) {
+                            hipStream_t s, const void *residual = nullptr) {
   (void)hipGetLastError();  // report only errors of the launches below
   Record rec{};
   bool timed = false;
@@ -229,7 +230,7 @@ static moe_status run_layer(const Plan &p, const void *u, const void *W_router, 
   err = p.path == PATH_TILED ? launch_down(p, W2, W2s, s) : launch_stream_down(p, W2, W2s, pk, s);
   if (err != hipSuccess) return fail();
   mark(4);
-  if (launch_combine(p, gates, y, s) != hipSuccess) return fail();
+  if (launch_combine(p, gates, residual, y, s) != hipSuccess) return fail();
   mark(5);
   if (timed) {
     std::lock_guard<std::mutex> lk(g_mu);
@@ -304,6 +305,98 @@ moe_status moe_layer_forward_packed(const void *u, const void *W_router, const f
   moe_shared sh{pk.gu_s, pk.gu_s, pk.dn_s};
   return run_layer(p, u, W_router, bias, nullptr, nullptr, nullptr, cfg->F_shared > 0 ? &sh : nullptr,
                    &pk, y, topk_idx, gates, static_cast<hipStream_t>(stream));
+}
+
+// ---- pre-norm residual block ----------------------------------------------
+
+static size_t elem_bytes(const moe_cfg &c) { return c.dtype == MOE_BF16 ? 2 : 4; }
+
+size_t moe_block_workspace_bytes(const moe_cfg *cfg) {
+  if (validate(cfg) != MOE_OK || cfg->d > rmsnorm_max_d()) return 0;
+  Plan p;
+  make_plan(*cfg, nullptr, &p);
+  return p.bytes + align_up(static_cast<size_t>(cfg->T) * cfg->d * elem_bytes(*cfg));
+}
+
+moe_status moe_rmsnorm(const void *h, const void *norm_weight, float eps, int64_t T, int32_t d, int32_t dtype,
+                       void *out, void *stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (T < 0 || d <= 0 || d % 64 != 0 || d > rmsnorm_max_d()) return MOE_ERR_SHAPE;
+  if (!std::isfinite(eps) || eps < 0.f) return MOE_ERR_CFG;
+  if (T == 0) return MOE_OK;
+  if (!h || !norm_weight || !out) return MOE_ERR_NULL;
+  if (!aligned16(h) || !aligned16(norm_weight) || !aligned16(out)) return MOE_ERR_ALIGN;
+  (void)hipGetLastError();
+  if (launch_rmsnorm(h, norm_weight, eps, T, d, dtype, out, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+// Checks the norm arguments and the larger workspace of the block; *un is
+// the normalised rows' place in the workspace (after the layer's buffers).
+static moe_status block_setup(const void *norm_weight, float eps, const moe_cfg *cfg, const Plan &p,
+                              void *workspace, size_t workspace_bytes, void **un) {
+  if (!norm_weight) return MOE_ERR_NULL;
+  if (!aligned16(norm_weight)) return MOE_ERR_ALIGN;
+  if (!std::isfinite(eps) || eps < 0.f) return MOE_ERR_CFG;
+  if (cfg->d > rmsnorm_max_d()) return MOE_ERR_SHAPE;
+  if (workspace_bytes < moe_block_workspace_bytes(cfg)) return MOE_ERR_WORKSPACE;
+  *un = static_cast<char *>(workspace) + p.bytes;
+  return MOE_OK;
+}
+
+moe_status moe_block_forward(const void *h, const void *norm_weight, float norm_eps, const void *W_router,
+                             const float *bias, const void *W1, const void *W3, const void *W2,
+                             const moe_shared *shared, const moe_cfg *cfg, void *y, int32_t *topk_idx,
+                             float *gates, void *workspace, size_t workspace_bytes, void *stream) {
+  moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if ((cfg->F_shared > 0) != (shared != nullptr)) return MOE_ERR_CFG;
+  if (cfg->T == 0) return MOE_OK;
+  if (!W1 || !W3 || !W2) return MOE_ERR_NULL;
+  if (shared && (!shared->W1 || !shared->W3 || !shared->W2)) return MOE_ERR_NULL;
+  const void *ptrs[] = {W1, W3, W2, shared ? shared->W1 : W1, shared ? shared->W3 : W1,
+                        shared ? shared->W2 : W1};
+  for (const void *q : ptrs)
+    if (!aligned16(q)) return MOE_ERR_ALIGN;
+  Plan p;
+  st = check_forward(h, W_router, cfg, y, topk_idx, gates, workspace, workspace_bytes, &p);
+  if (st != MOE_OK) return st;
+  void *un = nullptr;
+  st = block_setup(norm_weight, norm_eps, cfg, p, workspace, workspace_bytes, &un);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (launch_rmsnorm(h, norm_weight, norm_eps, cfg->T, cfg->d, cfg->dtype, un, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return run_layer(p, un, W_router, bias, W1, W3, W2, shared, nullptr, y, topk_idx, gates, s, h);
+}
+
+moe_status moe_block_forward_packed(const void *h, const void *norm_weight, float norm_eps, const void *W_router,
+                                    const float *bias, const void *packed, const moe_cfg *cfg, void *y,
+                                    int32_t *topk_idx, float *gates, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if (!packable(*cfg)) return MOE_ERR_SHAPE;
+  if (cfg->T == 0) return MOE_OK;
+  if (!packed) return MOE_ERR_NULL;
+  if (!aligned16(packed)) return MOE_ERR_ALIGN;
+  Plan p;
+  st = check_forward(h, W_router, cfg, y, topk_idx, gates, workspace, workspace_bytes, &p);
+  if (st != MOE_OK) return st;
+  if (p.path == PATH_TILED) return MOE_ERR_SHAPE;
+  void *un = nullptr;
+  st = block_setup(norm_weight, norm_eps, cfg, p, workspace, workspace_bytes, &un);
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (launch_rmsnorm(h, norm_weight, norm_eps, cfg->T, cfg->d, cfg->dtype, un, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  const PackedView pk = packed_view(*cfg, packed);
+  moe_shared sh{pk.gu_s, pk.gu_s, pk.dn_s};
+  return run_layer(p, un, W_router, bias, nullptr, nullptr, nullptr, cfg->F_shared > 0 ? &sh : nullptr, &pk, y,
+                   topk_idx, gates, s, h);
 }
 
 moe_status moe_balance_update(const int32_t *topk_idx, int64_t T, int32_t k, int32_t E, float gamma,

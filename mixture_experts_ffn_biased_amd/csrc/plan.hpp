@@ -97,7 +97,11 @@ hipError_t launch_permute(const Plan &p, const int32_t *topk_idx, hipStream_t s)
 hipError_t launch_gate_up(const Plan &p, const void *u, const void *W1, const void *W3,
                           const void *W1s, const void *W3s, hipStream_t s);
 hipError_t launch_down(const Plan &p, const void *W2, const void *W2s, hipStream_t s);
-hipError_t launch_combine(const Plan &p, const float *gates, void *y, hipStream_t s);
+// residual: optional [T][d] in the layer dtype, added to y last (the block form).
+hipError_t launch_combine(const Plan &p, const float *gates, const void *residual, void *y, hipStream_t s);
+int rmsnorm_max_d();
+hipError_t launch_rmsnorm(const void *h, const void *g, float eps, int64_t T, int d, int dtype, void *out,
+                          hipStream_t s);
 
 int stream_tile_m(int path);
 int stream_max_chunks();

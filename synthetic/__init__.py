@@ -18,6 +18,8 @@ Recipe (every tensor):
     a vector the caller passes in.
   * skewed layer: u_t = z_t + 2 m with m a seeded unit vector, and router row
     0 replaced by ``expert0_scale`` * m when the caller passes that scale.
+  * block form: u is the block input h; the RMSNorm weight is 1 + 0.1 N(0, 1)
+    (``make_norm_weight``, tensor id 10).
 
 The same (workload, seed, device) always gives the same tensors.  Draws on
 "cpu" and on "cuda" differ from each other; each test states which it uses.
@@ -31,7 +33,7 @@ from typing import Optional
 import torch
 
 TENSOR_IDS = {"u": 0, "W_router": 1, "W1": 2, "W3": 3, "W2": 4, "W1s": 5, "W3s": 6,
-              "W2s": 7, "bias": 8, "skew_dir": 9}
+              "W2s": 7, "bias": 8, "skew_dir": 9, "norm_weight": 10}
 
 
 @dataclass(frozen=True)
@@ -114,6 +116,14 @@ def _make_u(w: Workload, seed, dev):
         m = m / m.norm()
         u = u + w.skew_shift * m
     return u.to(torch_dtype(w)), m
+
+
+def make_norm_weight(w: Workload, seed: int = 0, device="cpu") -> torch.Tensor:
+    """RMSNorm weight of the block form: 1 + 0.1 N(0, 1) per hidden unit, in
+    the workload's dtype."""
+    dev = torch.device(device)
+    g = 1.0 + _randn((w.d,), _gen(seed, "norm_weight", dev), dev, 0.1, torch.float32)
+    return g.to(torch_dtype(w))
 
 
 def make_u(w: Workload, seed: int = 0, device="cpu") -> torch.Tensor:

@@ -157,3 +157,36 @@ def test_balance_update_arguments_are_checked_before_any_launch():
     assert call(g=float("nan")) == -3 and call(g=float("inf")) == -3
     assert call(b=None) == -1 and call(i=None) == -1
     assert call(b=f(0x20002)) == -7 and call(c=f(0x30001)) == -7
+
+
+def test_block_and_rmsnorm_arguments_are_checked_before_any_launch():
+    L = moe.lib()
+    f = ctypes.c_void_p
+    h, g, o = f(0x10000), f(0x20000), f(0x30000)
+    norm = lambda T=4, d=128, dt=1, eps=1e-6, hh=h, gg=g, oo=o: L.moe_rmsnorm(hh, gg, ctypes.c_float(eps), T, d, dt,
+                                                                               oo, None)
+    assert norm(dt=5) == -4
+    assert norm(d=100) == -2 and norm(d=8256) == -2 and norm(T=-1) == -2
+    assert norm(eps=-1.0) == -3 and norm(eps=float("nan")) == -3
+    assert norm(hh=None) == -1 and norm(gg=f(0x20008)) == -7
+    assert norm(T=0, hh=None, gg=None, oo=None) == 0  # no-op
+    c = cfg(n_groups=1, topk_groups=1)
+    layer = moe.moe_workspace_bytes(c)
+    blk = moe.moe_block_workspace_bytes(c)
+    assert blk >= layer + c.T * c.d * 2  # room for the normalised rows
+    assert moe.moe_block_workspace_bytes(cfg(E=0)) == 0
+    p = {n: f(0x10000 * (i + 1)) for i, n in enumerate(["h", "g", "Wr", "W1", "W3", "W2", "y", "idx", "gates",
+                                                          "ws"])}
+
+    def call(norm_weight=p["g"], eps=1e-6, ws_bytes=blk, cc=c):
+        x = cc.to_c()
+        return L.moe_block_forward(p["h"], norm_weight, ctypes.c_float(eps), p["Wr"], None, p["W1"], p["W3"],
+                                   p["W2"], None, ctypes.byref(x), p["y"], p["idx"], p["gates"], p["ws"],
+                                   ws_bytes, None)
+    assert call(norm_weight=None) == -1
+    assert call(norm_weight=f(0x20004)) == -7
+    assert call(eps=float("inf")) == -3
+    assert call(ws_bytes=layer) == -5  # enough for the layer, not for the block
+    x = c.to_c()
+    assert L.moe_block_forward_packed(p["h"], p["g"], ctypes.c_float(1e-6), p["Wr"], None, None,
+                                      ctypes.byref(x), p["y"], p["idx"], p["gates"], p["ws"], blk, None) == -2

@@ -1,0 +1,162 @@
+"""GPU parity of the pre-norm residual block, y = h + MoE(RMSNorm(h))
+("Lesson 2 -- From the Dense FFN to a Layer of Experts", section 2; "Sparse
+MoE FFN" (DeepSeek-V3), eq. 12), against the oracle.
+
+The GPU stores the normalised rows in the layer dtype before routing on them.
+moe_rmsnorm (the block's own kernel) is checked against the oracle's fp64
+RMSNorm to within one rounding of that dtype; the block is then checked
+against the oracle evaluated on those same rows, so both sides take the
+routing decisions on the same values."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_biased_amd as moe
+import oracle
+from oracle import block
+from parity import Y_TOL, host, mode_of, rel_l2, route_parity, sampled_outputs, widen_gpu
+from synthetic import WORKLOADS, Workload, make_inputs, make_norm_weight
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+
+SMALL = {
+    "sigmoid_groups_shared_bf16": Workload("sigmoid_groups_shared_bf16", 333, 256, 16, 4, 192, 128,
+                                           "sigmoid", 4, 2, 2.5, "bf16", "uniform"),
+    "tiny_fp32": WORKLOADS["tiny_fp32"],
+    "stream_sigmoid_groups_shared": Workload("stream_sigmoid_groups_shared", 1200, 512, 16, 4, 384, 256,
+                                             "sigmoid", 4, 2, 2.5, "bf16", "uniform"),
+    "decode_sigmoid_groups_shared": Workload("decode_sigmoid_groups_shared", 40, 256, 16, 4, 256, 256,
+                                             "sigmoid", 4, 2, 2.5, "bf16", "uniform"),
+}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.lib()
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("dtype,d,T", [("bf16", 7168, 257), ("bf16", 64, 5), ("f32", 512, 130), ("f32", 8192, 3)])
+def test_rmsnorm_matches_oracle(dev, dtype, d, T):
+    gen = torch.Generator(device="cpu").manual_seed(d + T)
+    scale = torch.exp(4 * torch.randn(T, 1, generator=gen))  # row scales over many decades
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    h = (torch.randn(T, d, generator=gen) * scale).to(tdt).to(dev)
+    g = (1 + 0.1 * torch.randn(d, generator=gen)).to(tdt).to(dev)
+    out = moe.moe_rmsnorm(h, g, EPS)
+    again = moe.moe_rmsnorm(h.clone(), g, EPS, out=None)
+    inplace = h.clone()
+    moe.moe_rmsnorm(inplace, g, EPS, out=inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again) and torch.equal(out, inplace)
+    ref = block.rmsnorm(host(h), host(g), EPS)
+    got = widen_gpu(out)
+    tol = 2.0 ** -8 if dtype == "bf16" else 4e-6  # one bf16 rounding / fp32 arithmetic
+    err = np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30)
+    assert err.max() <= tol, f"max relative error {err.max():.3e}"
+
+
+def block_both(w, inp, g, packed=None):
+    cfg = moe.MoeConfig.from_workload(w)
+    h = inp["u"]
+    if packed is None:
+        out = moe.moe_block_forward(h, g, EPS, inp["W_router"], inp["bias"], inp["W1"], inp["W3"], inp["W2"],
+                                    inp["shared"], cfg=cfg)
+    else:
+        out = moe.moe_block_forward_packed(h, g, EPS, inp["W_router"], inp["bias"], packed, cfg=cfg)
+    un = moe.moe_rmsnorm(h, g, EPS)
+    torch.cuda.synchronize()
+    return out, un
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_block_every_token(dev, name):
+    w = SMALL[name]
+    inp = make_inputs(w, seed=11, device=dev)
+    g = make_norm_weight(w, seed=11, device=dev)
+    (y, idx, gates), un = block_both(w, inp, g)
+    # the block routes and computes exactly as the layer on its normalised rows
+    cfg = moe.MoeConfig.from_workload(w)
+    yl, il, gl = moe.moe_layer_forward(un, inp["W_router"], inp["bias"], inp["W1"], inp["W3"], inp["W2"],
+                                       inp["shared"], cfg=cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, il) and torch.equal(gates, gl)
+    # against the oracle on those rows, with the residual
+    shared = None if inp["shared"] is None else tuple(host(s) for s in inp["shared"])
+    bias = None if inp["bias"] is None else inp["bias"].double().cpu().numpy()
+    kw = dict(bias=bias, shared=shared, score_fn=mode_of(w), n_groups=w.n_groups, topk_groups=w.topk_groups,
+              route_scale=w.route_scale)
+    yr, ir, gr, ge, gg = block.block_forward(host(inp["u"]), host(g), EPS, host(inp["W_router"]), host(inp["W1"]),
+                                             host(inp["W3"]), host(inp["W2"]), w.k, un=host(un), **kw)
+    lg = oracle.router_logits(host(un), host(inp["W_router"]))
+    gi = idx.cpu().numpy()
+    st = route_parity(w, gi, gates.cpu().numpy(), ir, gr, ge, gg, lg, bias)
+    diff = ~(np.sort(gi, 1) == np.sort(ir, 1)).all(1)
+    if diff.any():
+        t = np.nonzero(diff)[0]
+        sub = oracle.forward(oracle.widen(host(un))[t], host(inp["W_router"]), host(inp["W1"]), host(inp["W3"]),
+                             host(inp["W2"]), w.k, forced_idx=gi[t], **kw)
+        yr[t] = sub[0] + oracle.widen(host(inp["u"]))[t]
+    err = rel_l2(widen_gpu(y), yr)
+    assert err.max() <= Y_TOL[w.dtype], f"max rel-L2 {err.max():.3e}"
+    st["rel_l2_max"] = float(err.max())
+    log(f"[block] {name} {st}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_with_zero_down_projections_returns_its_input(dev, dtype):
+    w = SMALL["sigmoid_groups_shared_bf16"].with_(dtype=dtype)
+    inp = make_inputs(w, seed=3, device=dev)
+    inp["W2"].zero_()
+    inp["shared"][2].zero_()
+    g = make_norm_weight(w, seed=3, device=dev)
+    (y, _, _), _ = block_both(w, inp, g)
+    assert torch.equal(y, inp["u"])
+
+
+def test_block_packed_is_bitwise_the_plain_block(dev):
+    w = Workload("prefill_sigmoid_groups_shared", 900, 512, 16, 4, 256, 512, "sigmoid", 4, 2, 2.5, "bf16",
+                 "uniform")
+    inp = make_inputs(w, seed=5, device=dev)
+    g = make_norm_weight(w, seed=5, device=dev)
+    cfg = moe.MoeConfig.from_workload(w)
+    packed = moe.moe_pack_weights(inp["W1"], inp["W3"], inp["W2"], inp["shared"], cfg=cfg)
+    a, _ = block_both(w, inp, g)
+    b, _ = block_both(w, inp, g, packed=packed)
+    for x, z in zip(a, b):
+        assert torch.equal(x, z)
+
+
+def test_block_full_size_dsv3_prefill_packed(dev):
+    """The DeepSeek-V3-shaped prefill block (T = 8192) with packed weights, as
+    the benchmark runs it: routing of every token, outputs of sampled tokens."""
+    w = WORKLOADS["dsv3_prefill"]
+    inp = make_inputs(w, seed=0, device=dev)
+    g = make_norm_weight(w, seed=0, device=dev)
+    cfg = moe.MoeConfig.from_workload(w)
+    packed = moe.moe_pack_weights(inp["W1"], inp["W3"], inp["W2"], inp["shared"], cfg=cfg)
+    (y, idx, gates), un = block_both(w, inp, g, packed=packed)
+    del packed
+    bias = inp["bias"].double().cpu().numpy()
+    ir, gr, ge, gg, lg = oracle.route(host(un), host(inp["W_router"]), w.k, mode_of(w), w.n_groups,
+                                      w.topk_groups, w.route_scale, bias=bias)
+    gi = idx.cpu().numpy()
+    st = route_parity(w, gi, gates.cpu().numpy(), ir, gr, ge, gg, lg, bias)
+    tok = np.random.default_rng(0).choice(w.T, size=12, replace=False)
+    near = (ge < 1e-5) | (gg < 1e-5)
+    sel = np.where(near[tok, None], gi[tok], ir[tok])
+    yr, _, _ = sampled_outputs(w, dict(inp, u=un), tok, sel)
+    yr = yr + oracle.widen(host(inp["u"]))[tok]
+    err = rel_l2(widen_gpu(y[torch.from_numpy(tok).to(dev)]), yr)
+    assert err.max() <= Y_TOL[w.dtype], f"max rel-L2 {err.max():.3e}"
+    st["rel_l2_max"] = float(err.max())
+    log(f"[block] dsv3_prefill {st}")

@@ -389,3 +389,44 @@ def test_balance_step_hand_worked():
     b, c, _ = balance.update_step_fp32(idx, 16, b0, g)
     ref = balance.update_bias(b0.astype(np.float64), balance.usage(idx, 16), 500 * 4 / 16, float(g))
     assert np.array_equal(b, ref.astype(np.float32))
+
+
+def test_rmsnorm_closed_forms():
+    """RMSNorm ("Mixture of experts and architecture families": normalisation
+    without mean-centering; the pre-norm block of "Lesson 2 -- From the Dense
+    FFN to a Layer of Experts", section 2): x / sqrt(mean x^2 + eps) * g."""
+    from oracle import block
+    rng = np.random.default_rng(9)
+    g = rng.standard_normal(48)
+    # a constant row c normalises to sign(c) * g (eps = 0)
+    for c in (3.0, -0.25):
+        np.testing.assert_allclose(block.rmsnorm(np.full((1, 48), c), g, 0.0)[0], np.sign(c) * g, rtol=1e-15)
+    x = rng.standard_normal((5, 48))
+    # scale invariance at eps = 0, and unit mean square with g = 1
+    np.testing.assert_allclose(block.rmsnorm(7.5 * x, g, 0.0), block.rmsnorm(x, g, 0.0), rtol=1e-14)
+    n = block.rmsnorm(x, np.ones(48), 0.0)
+    np.testing.assert_allclose((n * n).mean(axis=1), 1.0, rtol=1e-14)
+    # eps keeps a zero row at zero; eps shrinks small rows: mean square = m / (m + eps)
+    assert np.array_equal(block.rmsnorm(np.zeros((1, 48)), g, 1e-6), np.zeros((1, 48)))
+    m = (x[0] ** 2).mean()
+    np.testing.assert_allclose((block.rmsnorm(x[:1], np.ones(48), 0.5) ** 2).mean(), m / (m + 0.5), rtol=1e-14)
+
+
+def test_block_residual_passes_through_when_the_experts_output_zero():
+    """y = h + MoE(RMSNorm(h)): with every down projection zero (routed and
+    shared) the block returns its input exactly."""
+    from oracle import block
+    rng = np.random.default_rng(10)
+    T, d, E, F = 12, 32, 4, 16
+    h = rng.standard_normal((T, d))
+    Wr = rng.standard_normal((E, d))
+    W1, W3 = rng.standard_normal((E, F, d)), rng.standard_normal((E, F, d))
+    shared = (rng.standard_normal((F, d)), rng.standard_normal((F, d)), np.zeros((d, F)))
+    y, idx, g, _, _ = block.block_forward(h, np.ones(d), 1e-6, Wr, W1, W3, np.zeros((E, d, F)), 2,
+                                          shared=shared)
+    assert np.array_equal(y, h)
+    # and the layer part is the layer on the normalised rows
+    W2 = rng.standard_normal((E, d, F))
+    y, idx, g, _, _ = block.block_forward(h, np.ones(d), 1e-6, Wr, W1, W3, W2, 2)
+    y0, idx0, g0, _, _ = oracle.forward(block.rmsnorm(h, np.ones(d), 1e-6), Wr, W1, W3, W2, 2)
+    assert np.array_equal(idx, idx0) and np.array_equal(y, y0 + h)
