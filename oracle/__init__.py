@@ -8,8 +8,9 @@ Three parts, all fp64:
 
 * ``moe_oracle.c`` (wrapped here through ctypes): the token-major layer as the
   pages define it -- router logits, scores, selection-only bias, group limit,
-  stable top-k, gates from raw scores, SwiGLU experts, unweighted shared
-  expert, gate-weighted sum -- plus the expert-contiguous permutation.
+  stable top-k, gates from raw scores, experts (SwiGLU, GEGLU, or the GELU
+  MLP with biases), unweighted shared expert, gate-weighted sum -- plus the
+  expert-contiguous permutation.
 * ``expert_major.py``: an independent second implementation that follows the
   expert-major masked loop of "Mixture of experts and architecture families",
   "The router and load balancing" (NumPy float64).
@@ -33,6 +34,10 @@ _LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 
 SOFTMAX = 0
 SIGMOID = 1
+
+SWIGLU = 0
+GEGLU = 1
+GELU_MLP = 2
 
 _F32, _BF16, _F64 = 0, 1, 2
 
@@ -66,6 +71,10 @@ def _load():
                                        P, I, P, P, P, P, P, P, P, P, I,
                                        P, P, P, P, P, P, I]
         lib.oracle_forward.restype = I
+        lib.oracle_forward_ex.argtypes = [I64, P, I, I, I, I, I, I, I, I, D,
+                                          P, I, P, P, I, P, P, P, P, P, P, P, P, P, P, I,
+                                          P, P, P, P, P, P, I]
+        lib.oracle_forward_ex.restype = I
         lib.oracle_permutation.argtypes = [I64, I, P, P, P, P, P]
         lib.oracle_permutation.restype = I
         _lib = lib
@@ -161,24 +170,47 @@ def route(u, W_router, k, score_fn=SOFTMAX, n_groups=1, topk_groups=1, route_sca
 
 def forward(u, W_router, W1, W3, W2, k, *, bias=None, shared=None, score_fn=SOFTMAX,
             n_groups=1, topk_groups=1, route_scale=1.0, tokens=None, forced_idx=None,
-            nthreads=None):
+            kind=SWIGLU, b1=None, b2=None, nthreads=None):
     """Whole-layer output for the listed tokens (None: all).
 
-    shared is None or (W1s [Fs][d], W3s [Fs][d], W2s [d][Fs]).
+    kind: SWIGLU (W2 (SiLU(W1 x) * W3 x)), GEGLU (GELU in place of SiLU) or
+    GELU_MLP (W2 GELU(W1 x + b1) + b2; W3 is None, b1 [E][F] / b2 [E][d] or
+    None for zero).
+    shared is None or (W1s [Fs][d], W3s [Fs][d] or None, W2s [d][Fs]
+    [, b1s [Fs], b2s [d]]).
     forced_idx [n][k] replaces selection (gates still come from raw scores).
     Returns (y fp64 [n][d], idx [n][k], gates [n][k], gap_expert [n], gap_group [n])."""
+    if kind not in (SWIGLU, GEGLU, GELU_MLP):
+        raise ValueError(f"unknown expert kind {kind}")
+    gated = kind != GELU_MLP
     u, Wr, W1, W3, W2 = _c(u), _c(W_router), _c(W1), _c(W3), _c(W2)
     T, d = u.shape
     E, F, d1 = W1.shape
-    assert d1 == d and W3.shape == W1.shape and W2.shape == (E, d, F) and Wr.shape == (E, d)
+    assert d1 == d and W2.shape == (E, d, F) and Wr.shape == (E, d)
+    assert (W3 is not None and W3.shape == W1.shape) if gated else W3 is None
+    if not gated:
+        b1, b2 = _c(b1), _c(b2)
+        assert b1 is None or b1.shape == (E, F)
+        assert b2 is None or b2.shape == (E, d)
+    elif b1 is not None or b2 is not None:
+        raise ValueError("biases belong to the GELU MLP expert only")
+    b1s = b2s = None
     if shared is not None:
-        W1s, W3s, W2s = (_c(a) for a in shared)
+        sh = tuple(_c(a) for a in shared)
+        W1s, W3s, W2s = sh[:3]
+        if len(sh) == 5:
+            b1s, b2s = sh[3:]
+            if gated and (b1s is not None or b2s is not None):
+                raise ValueError("biases belong to the GELU MLP expert only")
         Fs = W1s.shape[0]
-        assert W1s.shape == (Fs, d) and W3s.shape == (Fs, d) and W2s.shape == (d, Fs)
+        assert W1s.shape == (Fs, d) and W2s.shape == (d, Fs)
+        assert (W3s is not None and W3s.shape == (Fs, d)) if gated else W3s is None
+        assert b1s is None or b1s.shape == (Fs,)
+        assert b2s is None or b2s.shape == (d,)
     else:
         W1s = W3s = W2s = None
         Fs = 0
-    wcode = _check_weights(Wr, W1, W3, W2, W1s, W3s, W2s)
+    wcode = _check_weights(Wr, W1, W3, W2, W1s, W3s, W2s, b1, b2, b1s, b2s)
     tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64)
     n = T if tok is None else tok.shape[0]
     if tok is not None and n and (tok.min() < 0 or tok.max() >= T):
@@ -192,11 +224,11 @@ def forward(u, W_router, W1, W3, W2, k, *, bias=None, shared=None, score_fn=SOFT
     gates = np.empty((n, k), dtype=np.float64)
     ge = np.empty(n, dtype=np.float64)
     gg = np.empty(n, dtype=np.float64)
-    rc = _load().oracle_forward(n, _p(tok), d, E, k, F, Fs, score_fn, n_groups, topk_groups,
-                                float(route_scale), _p(u), _code(u), _p(Wr), _p(b),
-                                _p(W1), _p(W3), _p(W2), _p(W1s), _p(W3s), _p(W2s), wcode,
-                                _p(fi), _p(y), _p(idx), _p(gates), _p(ge), _p(gg),
-                                nthreads or default_threads())
+    rc = _load().oracle_forward_ex(n, _p(tok), d, E, k, F, Fs, score_fn, n_groups, topk_groups,
+                                   float(route_scale), _p(u), _code(u), _p(Wr), _p(b), kind,
+                                   _p(W1), _p(W3), _p(W2), _p(b1), _p(b2), _p(W1s), _p(W3s),
+                                   _p(W2s), _p(b1s), _p(b2s), wcode, _p(fi), _p(y), _p(idx),
+                                   _p(gates), _p(ge), _p(gg), nthreads or default_threads())
     if rc:
         raise ValueError("oracle_forward: invalid arguments")
     return y, idx, gates, ge, gg

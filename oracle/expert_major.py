@@ -13,22 +13,43 @@ softmax over that subset, so the two oracles must agree.
 The expert loop is the same page's masked loop: for each expert, take the rows
 whose selection contains it, run the expert on those rows, weight and add.
 Experts are SwiGLU ("Sparse MoE FFN" (DeepSeek-V3), "How it works"):
-W2 (SiLU(W1 x) * W3 x).
+W2 (SiLU(W1 x) * W3 x); or GEGLU, GELU in place of SiLU; or the biased GELU
+MLP of "Lesson 2 -- From the Dense FFN to a Layer of Experts", section 2:
+W2 GELU(W1 x + b1) + b2, with GELU(x) = x Phi(x) (SciPy's erf here).
 """
 from __future__ import annotations
 
 import numpy as np
+from scipy.special import erf
 
-from . import widen
+from . import GEGLU, GELU_MLP, SWIGLU, widen
 
 
 def silu(x):
     return x / (1.0 + np.exp(-x))
 
 
+def gelu(x):
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
 def swiglu(x, W1, W3, W2):
     """Rows x [n][d]; W1, W3 [F][d]; W2 [d][F] -> [n][d] (NumPy matmuls)."""
     return (silu(x @ W1.T) * (x @ W3.T)) @ W2.T
+
+
+def expert(x, kind, W1, W3, W2, b1=None, b2=None):
+    """One expert of the given body on rows x [n][d] -> [n][d]."""
+    if kind == SWIGLU:
+        return swiglu(x, W1, W3, W2)
+    if kind == GEGLU:
+        return (gelu(x @ W1.T) * (x @ W3.T)) @ W2.T
+    assert kind == GELU_MLP
+    a = x @ W1.T
+    if b1 is not None:
+        a = a + b1
+    o = gelu(a) @ W2.T
+    return o if b2 is None else o + b2
 
 
 def softmax_router(u, W_router, k):
@@ -42,12 +63,18 @@ def softmax_router(u, W_router, k):
     return idx.astype(np.int32), w
 
 
-def layer(u, W_router, W1, W3, W2, k, shared=None, idx=None, gates=None):
+def _w(a):
+    return None if a is None else widen(a)
+
+
+def layer(u, W_router, W1, W3, W2, k, shared=None, idx=None, gates=None, kind=SWIGLU,
+          b1=None, b2=None):
     """Expert-major layer output.  With idx/gates None the softmax router above
     chooses; otherwise the given selection and gates are used (so the expert
-    loop can also be checked under sigmoid, group-limited routing)."""
+    loop can also be checked under sigmoid, group-limited routing).
+    shared is (W1s, W3s, W2s[, b1s, b2s]); W3 is None for the GELU MLP."""
     u = widen(u)
-    W1, W3, W2 = widen(W1), widen(W3), widen(W2)
+    W1, W3, W2, b1, b2 = (_w(a) for a in (W1, W3, W2, b1, b2))
     if idx is None:
         idx, gates = softmax_router(u, widen(W_router), k)
     out = np.zeros_like(u)
@@ -56,8 +83,9 @@ def layer(u, W_router, W1, W3, W2, k, shared=None, idx=None, gates=None):
         rows = mask.any(axis=1)
         if rows.any():
             w = (gates * mask)[rows].sum(axis=1, keepdims=True)
-            out[rows] += w * swiglu(u[rows], W1[e], W3[e], W2[e])
+            out[rows] += w * expert(u[rows], kind, W1[e], None if W3 is None else W3[e], W2[e],
+                                    None if b1 is None else b1[e], None if b2 is None else b2[e])
     if shared is not None:
-        W1s, W3s, W2s = (widen(a) for a in shared)
-        out += swiglu(u, W1s, W3s, W2s)
+        sh = [_w(a) for a in shared] + [None] * (5 - len(shared))
+        out += expert(u, kind, *sh)
     return out, idx, gates

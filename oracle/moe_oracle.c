@@ -24,6 +24,11 @@
  *       softmax (softmax mode) or s / sum(s) (sigmoid mode), times
  *       route_scale ["The router in code"; "Sparse MoE FFN", Routing]
  *   - each expert is SwiGLU, W2 (SiLU(W1 u) * W3 u), SiLU(x) = x sigmoid(x)
+ *       ["Sparse MoE FFN", "How it works", expert equation]; the generic
+ *       expert of "Lesson 2 -- From the Dense FFN to a Layer of Experts",
+ *       section 2, W2 phi(W1 u + b1) + b2 with phi = GELU, and the gated unit
+ *       with GELU in place of SiLU (GEGLU) are the other two bodies
+ *       (oracle_forward_ex); GELU(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2
  *       ["Sparse MoE FFN", "How it works", expert equation]
  *   - y = sum_j g_j FFN_{i_j}(u) + FFN_shared(u), no residual, no dropping
  *       ["Sparse MoE FFN", eq. 12 and "Packed forward"]
@@ -48,6 +53,10 @@
 
 #define ORC_SOFTMAX 0
 #define ORC_SIGMOID 1
+
+#define ORC_SWIGLU 0
+#define ORC_GEGLU 1
+#define ORC_GELU_MLP 2
 
 /* ---- element access ------------------------------------------------------ */
 
@@ -110,6 +119,9 @@ typedef struct {
     const double *bias;      /* [E] or NULL (= zeros) */
     const void *W1, *W3, *W2;    /* [E][F][d], [E][F][d], [E][d][F] */
     const void *W1s, *W3s, *W2s; /* [Fs][d], [Fs][d], [d][Fs] or NULL */
+    int kind;                    /* ORC_SWIGLU, ORC_GEGLU, ORC_GELU_MLP */
+    const void *b1, *b2;         /* GELU MLP: [E][F], [E][d] or NULL (zero) */
+    const void *b1s, *b2s;       /* [Fs], [d] or NULL */
 } problem;
 
 /* ---- step 1: router logits ---------------------------------------------------- */
@@ -197,25 +209,39 @@ static void select_token(const select_cfg *S, const double *l, int32_t *idx,
 
 static double silu(double x) { return x / (1.0 + exp(-x)); }
 
-/* out[0..d) += scale * W2 (SiLU(W1 x) * W3 x); W1, W3 [F][d], W2 [d][F] at
- * element offsets off13 / off2 of the given arrays.  hbuf holds F doubles. */
-static void swiglu_accumulate(const double *x, int d, int F, const void *W1,
-                              const void *W3, const void *W2, int64_t off13,
-                              int64_t off2, int dtype, double scale,
+static double gelu(double x) { return 0.5 * x * (1.0 + erf(x / sqrt(2.0))); }
+
+/* One expert of the given body:
+ *   SwiGLU   h = SiLU(W1 x) * (W3 x)
+ *   GEGLU    h = GELU(W1 x) * (W3 x)
+ *   GELU MLP h = GELU(W1 x + b1)           (b1 NULL: zero)
+ * out[0..d) += scale * (W2 h + b2)          (b2 only for the GELU MLP)
+ * W1, W3 [F][d], W2 [d][F] at element offsets off13 / off2; b1, b2 at
+ * offsets offb1 / offb2.  hbuf holds F doubles. */
+static void expert_accumulate(const double *x, int d, int F, int kind, const void *W1,
+                              const void *W3, const void *W2, const void *b1,
+                              const void *b2, int64_t off13, int64_t off2,
+                              int64_t offb1, int64_t offb2, int dtype, double scale,
                               double *out, double *hbuf)
 {
     for (int f = 0; f < F; ++f) {
         double a = 0.0, c = 0.0;
         for (int j = 0; j < d; ++j) {
             a += elem(W1, off13 + (int64_t)f * d + j, dtype) * x[j];
-            c += elem(W3, off13 + (int64_t)f * d + j, dtype) * x[j];
+            if (kind != ORC_GELU_MLP) c += elem(W3, off13 + (int64_t)f * d + j, dtype) * x[j];
         }
-        hbuf[f] = silu(a) * c;
+        if (kind == ORC_SWIGLU)
+            hbuf[f] = silu(a) * c;
+        else if (kind == ORC_GEGLU)
+            hbuf[f] = gelu(a) * c;
+        else
+            hbuf[f] = gelu(a + (b1 ? elem(b1, offb1 + f, dtype) : 0.0));
     }
     for (int n = 0; n < d; ++n) {
         double o = 0.0;
         for (int f = 0; f < F; ++f)
             o += elem(W2, off2 + (int64_t)n * F + f, dtype) * hbuf[f];
+        if (kind == ORC_GELU_MLP && b2) o += elem(b2, offb2 + n, dtype);
         out[n] += scale * o;
     }
 }
@@ -396,34 +422,39 @@ static void forward_task(job *J, int64_t i, double *ds, int32_t *is)
     for (int n = 0; n < d; ++n) y[n] = 0.0;
     for (int j = 0; j < k; ++j) {
         int64_t e = idx[j];
-        swiglu_accumulate(x, d, P->F, P->W1, P->W3, P->W2, e * P->F * d,
-                          e * d * P->F, P->w_dtype, gates[j], y, h);
+        expert_accumulate(x, d, P->F, P->kind, P->W1, P->W3, P->W2, P->b1, P->b2,
+                          e * P->F * d, e * d * P->F, e * P->F, e * d, P->w_dtype,
+                          gates[j], y, h);
     }
     if (P->Fs > 0)
-        swiglu_accumulate(x, d, P->Fs, P->W1s, P->W3s, P->W2s, 0, 0, P->w_dtype,
-                          1.0, y, h);
+        expert_accumulate(x, d, P->Fs, P->kind, P->W1s, P->W3s, P->W2s, P->b1s, P->b2s,
+                          0, 0, 0, 0, P->w_dtype, 1.0, y, h);
 }
 
 /*
  * y[i][0..d), idx[i][0..k), gates[i][0..k) for the n tokens listed in tokens
  * (NULL: 0..n-1).  forced_idx [n][k] (or NULL) replaces steps 2-5.
- * Fs == 0 means no shared expert (W1s, W3s, W2s ignored).
+ * Fs == 0 means no shared expert (W1s, W3s, W2s ignored).  kind selects the
+ * expert body (ORC_SWIGLU, ORC_GEGLU, ORC_GELU_MLP); W3 / W3s are unused and
+ * b1, b2, b1s, b2s (NULL: zero) used only by the GELU MLP.
  * Returns 0, or -1 on an invalid argument.
  */
-int oracle_forward(int64_t n, const int64_t *tokens, int d, int E, int k,
-                   int F, int Fs, int score_fn, int n_groups, int topk_groups,
-                   double route_scale, const void *u, int u_dtype,
-                   const void *Wr, const double *bias, const void *W1,
-                   const void *W3, const void *W2, const void *W1s,
-                   const void *W3s, const void *W2s, int w_dtype,
-                   const int32_t *forced_idx, double *y, int32_t *idx,
-                   double *gates, double *gap_expert, double *gap_group,
-                   int nthreads)
+int oracle_forward_ex(int64_t n, const int64_t *tokens, int d, int E, int k,
+                      int F, int Fs, int score_fn, int n_groups, int topk_groups,
+                      double route_scale, const void *u, int u_dtype,
+                      const void *Wr, const double *bias, int kind, const void *W1,
+                      const void *W3, const void *W2, const void *b1, const void *b2,
+                      const void *W1s, const void *W3s, const void *W2s, const void *b1s,
+                      const void *b2s, int w_dtype, const int32_t *forced_idx, double *y,
+                      int32_t *idx, double *gates, double *gap_expert, double *gap_group,
+                      int nthreads)
 {
+    const int gated = kind == ORC_SWIGLU || kind == ORC_GEGLU;
+    if (kind != ORC_SWIGLU && kind != ORC_GEGLU && kind != ORC_GELU_MLP) return -1;
     if (check_select(E, k, score_fn, n_groups, topk_groups)) return -1;
     if (n < 0 || d <= 0 || F <= 0 || Fs < 0) return -1;
-    if (!u || !Wr || !W1 || !W3 || !W2 || !y || !idx || !gates) return -1;
-    if (Fs > 0 && (!W1s || !W3s || !W2s)) return -1;
+    if (!u || !Wr || !W1 || (gated && !W3) || !W2 || !y || !idx || !gates) return -1;
+    if (Fs > 0 && (!W1s || (gated && !W3s) || !W2s)) return -1;
     if (forced_idx)
         for (int64_t i = 0; i < n * k; ++i)
             if (forced_idx[i] < 0 || forced_idx[i] >= E) return -1;
@@ -448,6 +479,11 @@ int oracle_forward(int64_t n, const int64_t *tokens, int d, int E, int k,
     P.W1s = W1s;
     P.W3s = W3s;
     P.W2s = W2s;
+    P.kind = kind;
+    P.b1 = b1;
+    P.b2 = b2;
+    P.b1s = b1s;
+    P.b2s = b2s;
     select_cfg S = {E, k, score_fn, n_groups, topk_groups, route_scale, bias};
     job J = {0};
     J.P = &P;
@@ -466,6 +502,23 @@ int oracle_forward(int64_t n, const int64_t *tokens, int d, int E, int k,
     J.iscratch = 2 * (size_t)E;
     run_jobs(&J, nthreads);
     return 0;
+}
+
+/* The SwiGLU layer: oracle_forward_ex with kind ORC_SWIGLU. */
+int oracle_forward(int64_t n, const int64_t *tokens, int d, int E, int k,
+                   int F, int Fs, int score_fn, int n_groups, int topk_groups,
+                   double route_scale, const void *u, int u_dtype,
+                   const void *Wr, const double *bias, const void *W1,
+                   const void *W3, const void *W2, const void *W1s,
+                   const void *W3s, const void *W2s, int w_dtype,
+                   const int32_t *forced_idx, double *y, int32_t *idx,
+                   double *gates, double *gap_expert, double *gap_group,
+                   int nthreads)
+{
+    return oracle_forward_ex(n, tokens, d, E, k, F, Fs, score_fn, n_groups, topk_groups,
+                             route_scale, u, u_dtype, Wr, bias, ORC_SWIGLU, W1, W3, W2, NULL,
+                             NULL, W1s, W3s, W2s, NULL, NULL, w_dtype, forced_idx, y, idx,
+                             gates, gap_expert, gap_group, nthreads);
 }
 
 /* ---- exported: expert-contiguous permutation ---------------------------------------- */

@@ -307,6 +307,132 @@ def test_token_subset_and_forced_selection():
     np.testing.assert_array_equal(forced[2], full[2][tok])
 
 
+# ---------------------------------------------------------------- expert bodies
+
+# Standard normal CDF at 1 and 2 from printed tables: GELU(x) = x Phi(x).
+_PHI_1 = 0.8413447460685429
+_PHI_2 = 0.9772498680518208
+
+
+def test_gelu_mlp_closed_form_with_per_expert_biases():
+    """Diagonal W1, identity W2, one forced expert per token: the layer is
+    GELU(a_e x + b1_e) + b2_e elementwise, with the gate of a single chosen
+    expert equal to 1 (softmax over the k chosen)."""
+    from scipy.stats import norm
+    E, d = 4, 6
+    a = np.array([[1.0, 0.5, -1.0, 2.0, 0.0, 1.5],
+                  [2.0, 1.0, 1.0, -0.5, 3.0, 0.25],
+                  [-2.0, 1.0, 0.75, 1.0, -1.0, 1.0],
+                  [1.0, 1.0, 1.0, 1.0, 1.0, 1.0]])
+    b1 = np.arange(E * d, dtype=np.float64).reshape(E, d) * 0.05 - 0.4
+    b2 = np.arange(E * d, dtype=np.float64).reshape(E, d)[:, ::-1] * 0.1 - 1.0
+    W1 = np.stack([np.diag(r) for r in a])
+    W2 = np.stack([np.eye(d)] * E)
+    u = np.array([[1.0, -1.0, 0.5, 2.0, -0.3, 0.0],
+                  [0.2, 0.4, -2.0, 1.0, 1.0, -1.5],
+                  [1.0, 1.0, 1.0, 1.0, 1.0, 1.0],
+                  [-0.7, 2.2, 0.1, -1.1, 0.9, 0.3],
+                  [0.0, 0.0, 0.0, 0.0, 0.0, 0.0]])
+    Wr = np.zeros((E, d))
+    forced = np.array([[2], [0], [3], [1], [2]], dtype=np.int32)
+    y, idx, g, _, _ = oracle.forward(u, Wr, W1, None, W2, 1, kind=oracle.GELU_MLP, b1=b1,
+                                     b2=b2, forced_idx=forced)
+    assert (g == 1.0).all()
+    e = forced[:, 0]
+    z = a[e] * u + b1[e]
+    np.testing.assert_allclose(y, z * norm.cdf(z) + b2[e], rtol=1e-14, atol=1e-15)
+    # row 2 (expert 3: a = 1): the pre-activation is 1 + b1[3]; check the
+    # printed table values where the argument lands on 1 or 2 exactly
+    u1 = np.array([[1.0 - b1[3, 0], 2.0 - b1[3, 1], -1.0 - b1[3, 2], 0.0, 0.0, 0.0]])
+    y1, _, _, _, _ = oracle.forward(u1, Wr, W1, None, W2, 1, kind=oracle.GELU_MLP, b1=b1,
+                                    b2=np.zeros_like(b2), forced_idx=np.array([[3]], np.int32))
+    np.testing.assert_allclose(y1[0, :3], [_PHI_1, 2 * _PHI_2, -(1 - _PHI_1)], rtol=1e-14)
+
+
+def test_geglu_closed_form():
+    from scipy.stats import norm
+    E, d = 3, 5
+    rng = np.random.default_rng(21)
+    a = rng.uniform(-2, 2, (E, d))
+    c = rng.uniform(-2, 2, (E, d))
+    W1 = np.stack([np.diag(r) for r in a])
+    W3 = np.stack([np.diag(r) for r in c])
+    W2 = np.stack([np.eye(d)] * E)
+    u = rng.standard_normal((7, d))
+    forced = (np.arange(7, dtype=np.int32) % E)[:, None]
+    y, _, g, _, _ = oracle.forward(u, np.zeros((E, d)), W1, W3, W2, 1, kind=oracle.GEGLU,
+                                   forced_idx=forced)
+    e = forced[:, 0]
+    z = a[e] * u
+    np.testing.assert_allclose(y, z * norm.cdf(z) * (c[e] * u), rtol=1e-13, atol=1e-15)
+
+
+def _torch_gelu_mlp(x, W1, W2, b1, b2):
+    x, W1, W2, b1, b2 = (torch.from_numpy(oracle.widen(t)) for t in (x, W1, W2, b1, b2))
+    return (torch.nn.functional.gelu(x @ W1.T + b1) @ W2.T + b2).numpy()
+
+
+def test_gelu_mlp_k_equals_E_weights_the_output_bias_by_the_gate():
+    """k = E: y = sum_e p_e (W2_e GELU(W1_e x + b1_e) + b2_e), p the softmax of
+    the logits (PyTorch's exact GELU)."""
+    rng = np.random.default_rng(22)
+    T, d, E, F = 20, 12, 4, 16
+    u, Wr, W1, _, W2, _ = _rand_layer(rng, T, d, E, F)
+    b1 = rng.standard_normal((E, F)) * 0.3
+    b2 = rng.standard_normal((E, d)) * 0.3
+    y, _, _, _, _ = oracle.forward(u, Wr, W1, None, W2, E, kind=oracle.GELU_MLP, b1=b1, b2=b2)
+    p = torch.softmax(torch.from_numpy(u @ Wr.T), dim=1).numpy()
+    ref = sum(p[:, e:e + 1] * _torch_gelu_mlp(u, W1[e], W2[e], b1[e], b2[e]) for e in range(E))
+    np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_gelu_mlp_shared_expert_with_biases_is_added_unweighted():
+    rng = np.random.default_rng(23)
+    T, d, E, F, Fs = 24, 16, 8, 12, 20
+    u, Wr, W1, _, W2, _ = _rand_layer(rng, T, d, E, F)
+    W1s = rng.standard_normal((Fs, d)) / 4
+    W2s = rng.standard_normal((d, Fs)) / 4
+    b1s = rng.standard_normal(Fs) * 0.2
+    b2s = rng.standard_normal(d) * 0.2
+    y, _, _, _, _ = oracle.forward(u, Wr, W1, None, np.zeros_like(W2), 3, kind=oracle.GELU_MLP,
+                                   shared=(W1s, None, W2s, b1s, b2s), score_fn=oracle.SIGMOID,
+                                   n_groups=4, topk_groups=2, route_scale=2.5)
+    np.testing.assert_allclose(y, _torch_gelu_mlp(u, W1s, W2s, b1s, b2s), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("kind", [oracle.GEGLU, oracle.GELU_MLP])
+def test_token_major_matches_expert_major_other_bodies(kind):
+    rng = np.random.default_rng(24 + kind)
+    arrs = _rand_layer(rng, 64, 32, 16, 24, Fs=16, dtype=np.float32)
+    to_bf16 = lambda a: (a.view(np.uint32) >> 16).astype(np.uint16)
+    u, Wr, W1, W3, W2 = (to_bf16(a) for a in arrs[:5])
+    W1s, W3s, W2s = (to_bf16(a) for a in arrs[5])
+    b1 = b2 = b1s = b2s = None
+    if kind == oracle.GELU_MLP:
+        W3 = W3s = None
+        b1 = to_bf16(rng.standard_normal((16, 24)).astype(np.float32) * 0.2)
+        b2 = to_bf16(rng.standard_normal((16, 32)).astype(np.float32) * 0.2)
+        b1s = to_bf16(rng.standard_normal(16).astype(np.float32) * 0.2)
+        b2s = to_bf16(rng.standard_normal(32).astype(np.float32) * 0.2)
+    shared = (W1s, W3s, W2s, b1s, b2s)
+    bias = rng.uniform(-0.05, 0.05, 16)
+    y, idx, g, _, _ = oracle.forward(u, Wr, W1, W3, W2, 4, bias=bias, shared=shared,
+                                     score_fn=oracle.SIGMOID, n_groups=4, topk_groups=2,
+                                     route_scale=2.5, kind=kind, b1=b1, b2=b2)
+    ref, _, _ = expert_major.layer(u, Wr, W1, W3, W2, 4, shared=shared, idx=idx, gates=g,
+                                   kind=kind, b1=b1, b2=b2)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_expert_kind_argument_checks():
+    rng = np.random.default_rng(25)
+    u, Wr, W1, W3, W2, _ = _rand_layer(rng, 4, 8, 2, 8)
+    with pytest.raises(ValueError):
+        oracle.forward(u, Wr, W1, W3, W2, 1, kind=7)
+    with pytest.raises(ValueError):
+        oracle.forward(u, Wr, W1, W3, W2, 1, b1=np.zeros((2, 8)))
+
+
 # ---------------------------------------------------------------- permutation
 
 def test_permutation_is_the_stable_expert_order():
