@@ -149,6 +149,62 @@ moe_status moe_layer_forward_packed(const void *u, const void *W_router, const f
                                     void *stream);
 
 /*
+ * Other expert bodies.  "Lesson 2 -- From the Dense FFN to a Layer of
+ * Experts", section 2, writes each expert as the dense FFN it replaces, an
+ * activation between two affine maps with biases, GELU or a gated unit; the
+ * cheat sheet ("Mixture of Experts and Hybrid Architectures", "Calculator
+ * defaults") takes GELU as the default activation and names SwiGLU and GEGLU
+ * as the gated ones, which add the third matrix W3.
+ * GELU(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2, the exact form (erff in
+ * fp32).
+ *
+ *   MOE_EXPERT_SWIGLU    FFN(x) = W2 (SiLU(W1 x) * W3 x)     (= moe_layer_forward)
+ *   MOE_EXPERT_GEGLU     FFN(x) = W2 (GELU(W1 x) * W3 x)
+ *   MOE_EXPERT_GELU_MLP  FFN(x) = W2 GELU(W1 x + b1) + b2
+ *
+ * The gate weights the whole expert output, b2 included; the shared expert,
+ * of the same body with its own biases, is added unweighted.
+ *
+ * moe_experts (every tensor device memory in cfg->dtype, 16-byte aligned):
+ *   W1, W3 [E][F][d], W2 [E][d][F]; b1 [E][F], b2 [E][d]
+ *   W1s, W3s [F_shared][d], W2s [d][F_shared]; b1s [F_shared], b2s [d]
+ *   W3 / W3s are not read by the GELU MLP (may be NULL); the biases belong to
+ *   the GELU MLP only (NULL there == zero; non-NULL with a gated kind is
+ *   MOE_ERR_CFG).  The shared pointers must be NULL iff cfg->F_shared == 0
+ *   (else MOE_ERR_CFG), biases aside.
+ * moe_workspace_bytes_ex: workspace for cfg with experts of the given kind,
+ *   0 when cfg or kind is invalid (for SwiGLU, moe_workspace_bytes(cfg)).
+ * moe_plan_describe_ex: moe_plan_describe for the given kind.  The GELU MLP
+ *   takes the streaming kernels only with F % 256 == 0 and F_shared % 256 == 0.
+ * moe_layer_forward_ex: moe_layer_forward with these experts (plain layout;
+ *   the packed layout serves SwiGLU only).  For bf16 the hidden activations
+ *   after the activation (and the bias b1) and the per-slot expert outputs
+ *   (with b2) are stored as bf16.  MOE_ERR_DTYPE for an unknown kind.
+ */
+typedef enum { MOE_EXPERT_SWIGLU = 0, MOE_EXPERT_GEGLU = 1, MOE_EXPERT_GELU_MLP = 2 } moe_expert_kind;
+
+typedef struct {
+    int32_t kind;     /* moe_expert_kind */
+    const void *W1;
+    const void *W3;
+    const void *W2;
+    const void *b1;
+    const void *b2;
+    const void *W1s;
+    const void *W3s;
+    const void *W2s;
+    const void *b1s;
+    const void *b2s;
+} moe_experts;
+
+size_t moe_workspace_bytes_ex(const moe_cfg *cfg, int32_t kind);
+moe_status moe_plan_describe_ex(const moe_cfg *cfg, int32_t kind, int32_t *gemm_path, int32_t *tile_rows);
+moe_status moe_layer_forward_ex(const void *u, const void *W_router, const float *bias,
+                                const moe_experts *experts, const moe_cfg *cfg, void *y,
+                                int32_t *topk_idx, float *gates, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
  * Routing and permutation only (the first two stages of moe_layer_forward,
  * same kernels), for tests and tools.  Outputs, all int32 device arrays:
  *   counts [E]       slots that chose expert e
@@ -240,8 +296,8 @@ const char *moe_status_str(int status);
  * moe_timing_read synchronises on the recorded events, adds the elapsed
  * milliseconds of each stage into ms[MOE_N_STAGES], stores the number of
  * calls measured in *calls, and (reset != 0) clears the records.
- * Stages: 0 router+top-k, 1 permutation, 2 gate/up projections with SiLU*mul,
- * 3 down projections, 4 gate-weighted combine.
+ * Stages: 0 router+top-k, 1 permutation, 2 gate/up projections with the
+ * activation, 3 down projections, 4 gate-weighted combine.
  */
 #define MOE_N_STAGES 5
 moe_status moe_timing_enable(int on);

@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_EXPERT_SWIGLU, MOE_EXPERT_GEGLU, MOE_EXPERT_GELU_MLP = 0, 1, 2
+EXPERT_KINDS = {"swiglu": MOE_EXPERT_SWIGLU, "geglu": MOE_EXPERT_GEGLU, "gelu_mlp": MOE_EXPERT_GELU_MLP}
 MOE_N_STAGES = 5
 STAGES = ("router_topk", "permute", "gate_up", "down", "combine")
 
@@ -43,6 +45,11 @@ class moe_cfg(ctypes.Structure):
 
 class moe_shared(ctypes.Structure):
     _fields_ = [("W1", ctypes.c_void_p), ("W3", ctypes.c_void_p), ("W2", ctypes.c_void_p)]
+
+
+class moe_experts(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32)] + [
+        (n, ctypes.c_void_p) for n in ("W1", "W3", "W2", "b1", "b2", "W1s", "W3s", "W2s", "b1s", "b2s")]
 
 
 @dataclass(frozen=True)
@@ -122,6 +129,13 @@ def lib():
         L.moe_plan_describe.argtypes = [CP, ctypes.POINTER(ctypes.c_int32),
                                         ctypes.POINTER(ctypes.c_int32)]
         L.moe_plan_describe.restype = I32
+        L.moe_workspace_bytes_ex.argtypes = [CP, I32]
+        L.moe_workspace_bytes_ex.restype = SZ
+        L.moe_plan_describe_ex.argtypes = [CP, I32, ctypes.POINTER(ctypes.c_int32),
+                                           ctypes.POINTER(ctypes.c_int32)]
+        L.moe_plan_describe_ex.restype = I32
+        L.moe_layer_forward_ex.argtypes = [P, P, P, ctypes.POINTER(moe_experts), CP, P, P, P, P, SZ, P]
+        L.moe_layer_forward_ex.restype = I32
         L.moe_status_str.argtypes = [I32]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_timing_enable.argtypes = [I32]
@@ -157,6 +171,25 @@ def moe_plan_describe(cfg: MoeConfig):
 def moe_workspace_bytes(cfg: MoeConfig) -> int:
     c = cfg.to_c()
     return int(lib().moe_workspace_bytes(ctypes.byref(c)))
+
+
+def _kind(kind) -> int:
+    return EXPERT_KINDS[kind] if isinstance(kind, str) else int(kind)
+
+
+def moe_workspace_bytes_ex(cfg: MoeConfig, kind) -> int:
+    c = cfg.to_c()
+    return int(lib().moe_workspace_bytes_ex(ctypes.byref(c), _kind(kind)))
+
+
+def moe_plan_describe_ex(cfg: MoeConfig, kind):
+    """moe_plan_describe for experts of the given kind ("swiglu", "geglu", "gelu_mlp")."""
+    c = cfg.to_c()
+    path, rows = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    st = lib().moe_plan_describe_ex(ctypes.byref(c), _kind(kind), ctypes.byref(path), ctypes.byref(rows))
+    if st != 0:
+        raise MoeError(st, "moe_plan_describe_ex")
+    return GEMM_PATHS[path.value], rows.value
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -228,6 +261,65 @@ def moe_layer_forward(u, W_router, bias, W1, W3, W2, shared: Optional[Sequence] 
                                  workspace.numel(), _stream(dev, stream))
     if st != 0:
         raise MoeError(st, "moe_layer_forward")
+    return y, topk_idx, gates
+
+
+def moe_layer_forward_ex(u, W_router, bias, kind, W1, W3, W2, b1=None, b2=None, shared=None, *,
+                         cfg: MoeConfig, y=None, topk_idx=None, gates=None, workspace=None, stream=None):
+    """moe_layer_forward with experts of the given kind ("swiglu", "geglu", "gelu_mlp").
+
+    W3 is None for the GELU MLP; b1 [E][F] and b2 [E][d] (GELU MLP only) may be None.
+    shared: None or (W1s, W3s, W2s[, b1s, b2s])."""
+    kd = _kind(kind)
+    dev = u.device
+    dt = cfg.torch_dtype
+    T, d, E, k, F, Fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.F_shared
+    _need(u, (T, d), dt, "u", dev)
+    _need(W_router, (E, d), dt, "W_router", dev)
+    _need(W1, (E, F, d), dt, "W1", dev)
+    if W3 is not None:
+        _need(W3, (E, F, d), dt, "W3", dev)
+    _need(W2, (E, d, F), dt, "W2", dev)
+    if b1 is not None:
+        _need(b1, (E, F), dt, "b1", dev)
+    if b2 is not None:
+        _need(b2, (E, d), dt, "b2", dev)
+    if bias is not None:
+        _need(bias, (E,), torch.float32, "bias", dev)
+    ex = moe_experts(kd, *(None if t is None else t.data_ptr() for t in (W1, W3, W2, b1, b2)))
+    if shared is not None:
+        sh = list(shared) + [None] * (5 - len(shared))
+        W1s, W3s, W2s, b1s, b2s = sh
+        _need(W1s, (Fs, d), dt, "W1s", dev)
+        if W3s is not None:
+            _need(W3s, (Fs, d), dt, "W3s", dev)
+        _need(W2s, (d, Fs), dt, "W2s", dev)
+        if b1s is not None:
+            _need(b1s, (Fs,), dt, "b1s", dev)
+        if b2s is not None:
+            _need(b2s, (d,), dt, "b2s", dev)
+        for name, t in zip(("W1s", "W3s", "W2s", "b1s", "b2s"), sh):
+            setattr(ex, name, None if t is None else t.data_ptr())
+    if y is None:
+        y = torch.empty((T, d), dtype=dt, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if gates is None:
+        gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(y, (T, d), dt, "y", dev)
+    _need(topk_idx, (T, k), torch.int32, "topk_idx", dev)
+    _need(gates, (T, k), torch.float32, "gates", dev)
+    if workspace is None:
+        n = moe_workspace_bytes_ex(cfg, kd)
+        if n == 0 and T > 0:
+            raise MoeError(moe_check_cfg(cfg) or -4, "moe_workspace_bytes_ex")
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    c = cfg.to_c()
+    st = lib().moe_layer_forward_ex(_ptr(u), _ptr(W_router), _ptr(bias), ctypes.byref(ex), ctypes.byref(c),
+                                    _ptr(y), _ptr(topk_idx), _ptr(gates), _ptr(workspace), workspace.numel(),
+                                    _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_layer_forward_ex")
     return y, topk_idx, gates
 
 

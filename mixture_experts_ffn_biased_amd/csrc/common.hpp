@@ -30,6 +30,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
+// GELU(x) = x Phi(x), Phi the standard normal CDF, through erf (exact form).
+__device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
 // Total order used by top-k: larger score first, then lower index; NaN ranks
 // below every number; -0 and +0 tie.  The 64-bit key is compared as an
 // unsigned integer; 0 is reserved for "no candidate".

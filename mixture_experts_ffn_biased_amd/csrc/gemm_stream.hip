@@ -1,10 +1,11 @@
 // Grouped expert GEMMs on gfx950 for bf16 layers: persistent, XCD-aware,
 // weight-streaming kernels.
 //
-// Same two products as grouped_gemm.hip (the SwiGLU expert of "Sparse MoE
-// FFN" (DeepSeek-V3), "How it works", batched as grouped GEMMs as "Mixture of
-// experts and architecture families", "The router and load balancing",
-// suggests); only the schedule and the data movement differ:
+// Same two products and epilogues as grouped_gemm.hip (the SwiGLU expert of
+// "Sparse MoE FFN" (DeepSeek-V3), "How it works", or the GEGLU and biased
+// GELU-MLP bodies, batched as grouped GEMMs as "Mixture of experts and
+// architecture families", "The router and load balancing", suggests); only
+// the schedule and the data movement differ:
 //
 //  * One workgroup per CU loops over work items (tile, n-slab).  Items are
 //    kept in eight per-XCD lists: a chunk (up to two tiles of one expert)
@@ -26,9 +27,11 @@
 //  * Decode variant (few rows per expert): 32-row tiles, 4 waves each 32 x 64,
 //    an 8-slot ring (7 x 16 KB of weights in flight): a weight stream with a
 //    small MFMA on the side.
-//  * gate_up: each wave column's 64 weight rows are 32 rows of W1 then the
-//    same 32 of W3, so SiLU(x W1^T) * (x W3^T) meets in the same lane; the
-//    bf16 result goes through LDS to 16-byte stores.
+//  * gate_up of the gated bodies: each wave column's 64 weight rows are 32
+//    rows of W1 then the same 32 of W3, so act(x W1^T) * (x W3^T) meets in
+//    the same lane; the bf16 result goes through LDS to 16-byte stores.  The
+//    GELU MLP's gate_up is a single product like down (256 W1 rows a slab),
+//    with bias and GELU in the epilogue.
 //  * Weights are read either in their plain [rows][K] layout or packed once
 //    (moe_pack_weights) so that each stage's 16 KB weight tile is contiguous
 //    in memory in exactly the order it lands in LDS.
@@ -74,6 +77,8 @@ struct StreamArgs {
   const void *Bp_routed, *Bp_shared;  // packed layout: stage blocks of each slab
   int N_routed, N_shared, K_routed, K_shared;
   void *C_routed, *C_shared;
+  const void *bias_routed;  // [E][N] or null (EPI_BIAS, EPI_BIAS_GELU)
+  const void *bias_shared;  // [N] or null
 };
 
 template <int NS>
@@ -183,9 +188,10 @@ __device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Pt
   Rem<NS, PS, NS, 0>::run(ring, G * NS, issue, compute);
 }
 
-template <bool DUAL, bool PACKED, int VAR>
+template <int EPI, bool PACKED, int VAR>
 __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const Ring<V<VAR>::NSTAGE> &ring) {
   constexpr int BM = V<VAR>::BM, NT = V<VAR>::NT;
+  constexpr bool DUAL = epi_dual(EPI);
   const Tile tl = g.tiles[item.x];
   const bool shared = tl.group == g.E;
   const int N = shared ? g.N_shared : g.N_routed;
@@ -298,7 +304,8 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
       for (int r = 0; r < 16; ++r) {
         const int row = mi * 32 + 8 * (r >> 2) + row_lane + (r & 3);
         const int col = wn * 32 + (lane & 31);
-        Ht[row * 128 + col] = f32_to_bf16(silu(acc[mi][0][r]) * acc[mi][1][r]);
+        const float a1 = acc[mi][0][r];
+        Ht[row * 128 + col] = f32_to_bf16((EPI == EPI_GELU_GLU ? gelu(a1) : silu(a1)) * acc[mi][1][r]);
       }
     }
     __syncthreads();
@@ -315,6 +322,15 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   } else {
     // Output tile: BM x 256 bf16 (512 bytes a row); rows 64*s .. 64*s+63 in
     // slot s (the decode tile's 32 rows all in slot 0).
+    float bv[2] = {0.f, 0.f};
+    if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
+      const uint16_t *bias = static_cast<const uint16_t *>(shared ? g.bias_shared : g.bias_routed);
+      if (bias) {
+        if (!shared) bias += static_cast<int64_t>(tl.group) * N;
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) bv[ni] = bf16_to_f32(bias[n0 + wn * 64 + ni * 32 + (lane & 31)]);
+      }
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       if (mi >= nmi) break;
@@ -326,7 +342,10 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
         for (int r = 0; r < 16; ++r) {
           const int row = (mi & 1) * 32 + 8 * (r >> 2) + row_lane + (r & 3);
           const int col = wn * 64 + ni * 32 + (lane & 31);
-          Ot[row * 256 + col] = f32_to_bf16(acc[mi][ni][r]);
+          float v = acc[mi][ni][r];
+          if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) v += bv[ni];
+          if (EPI == EPI_BIAS_GELU) v = gelu(v);
+          Ot[row * 256 + col] = f32_to_bf16(v);
         }
     }
     __syncthreads();
@@ -346,7 +365,7 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
 
 // The ring is idle between items, so the fetched item index is broadcast
 // through the first word of slot 0.
-template <bool DUAL, bool PACKED, int VAR>
+template <int EPI, bool PACKED, int VAR>
 __device__ __forceinline__ void item_loop(const StreamArgs &g, const Ring<V<VAR>::NSTAGE> &ring) {
   int *item_sh = reinterpret_cast<int *>(ring.s[0]);
   const int xcd = blockIdx.x & 7;
@@ -360,14 +379,14 @@ __device__ __forceinline__ void item_loop(const StreamArgs &g, const Ring<V<VAR>
       const int it = *item_sh;
       __syncthreads();
       if (it >= cnt) break;
-      run_item<DUAL, PACKED, VAR>(g, g.items[off + it], ring);
+      run_item<EPI, PACKED, VAR>(g, g.items[off + it], ring);
     }
   }
 }
 
 // Separate __shared__ ring slots: the compiler can then tell the LDS loads
 // into one slot from the reads of another and adds no waits of its own.
-template <bool DUAL, bool PACKED>
+template <int EPI, bool PACKED>
 __global__ __launch_bounds__(512, 1) void gemm_stream_prefill(StreamArgs g) {
   constexpr int SB = stage_bytes<0>();
   __shared__ __attribute__((aligned(16))) unsigned char r0[SB], r1[SB], r2[SB], r3[SB];
@@ -376,10 +395,10 @@ __global__ __launch_bounds__(512, 1) void gemm_stream_prefill(StreamArgs g) {
   ring.s[1] = r1;
   ring.s[2] = r2;
   ring.s[3] = r3;
-  item_loop<DUAL, PACKED, 0>(g, ring);
+  item_loop<EPI, PACKED, 0>(g, ring);
 }
 
-template <bool DUAL, bool PACKED>
+template <int EPI, bool PACKED>
 __global__ __launch_bounds__(256, 1) void gemm_stream_decode(StreamArgs g) {
   constexpr int SB = stage_bytes<1>();
   __shared__ __attribute__((aligned(16))) unsigned char r0[SB], r1[SB], r2[SB], r3[SB], r4[SB], r5[SB],
@@ -393,7 +412,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_decode(StreamArgs g) {
   ring.s[5] = r5;
   ring.s[6] = r6;
   ring.s[7] = r7;
-  item_loop<DUAL, PACKED, 1>(g, ring);
+  item_loop<EPI, PACKED, 1>(g, ring);
 }
 
 // ---- one-time weight packing -------------------------------------------------
@@ -569,7 +588,8 @@ int stream_tile_m(int path) { return path == PATH_STREAM_DECODE ? V<1>::BM : V<0
 // and read each slab together.
 int stream_tile_balanced(int path) { return path == PATH_STREAM ? 1 : 0; }
 int stream_max_chunks() { return kMaxChunks; }
-int stream_nslab_gate_up(int F) { return F / (SBN / 2); }
+// Gated bodies: 128 columns of W1 and W3 a slab; the GELU MLP: 256 of W1.
+int stream_nslab_gate_up(int F, int kind) { return kind == MOE_EXPERT_GELU_MLP ? F / SBN : F / (SBN / 2); }
 int stream_nslab_down(int d) { return d / SBN; }
 
 size_t packed_weights_bytes(const moe_cfg &c) {
@@ -609,70 +629,92 @@ hipError_t launch_pack_weights(const moe_cfg &c, const void *W1, const void *W3,
 hipError_t launch_stream_schedule(const Plan &p, hipStream_t s) {
   const moe_cfg &c = p.cfg;
   hipLaunchKernelGGL(stream_schedule, dim3(1), dim3(256), 0, s, p.counts, c.E, c.T, c.F_shared > 0 ? 1 : 0,
-                     p.tile_m, c.F / (SBN / 2), c.F_shared / (SBN / 2), c.d / SBN, c.d / SBN, p.items_gu,
+                     p.tile_m, stream_nslab_gate_up(c.F, p.kind), stream_nslab_gate_up(c.F_shared, p.kind),
+                     c.d / SBN, c.d / SBN, p.items_gu,
                      p.items_dn, p.sched_meta);
   return hipGetLastError();
 }
 
-static hipError_t launch_stream(const Plan &p, const StreamArgs &a, bool dual, bool packed, hipStream_t s) {
-  typedef void (*kernel_t)(StreamArgs);
-  kernel_t k;
-  int threads;
-  if (p.path == PATH_STREAM_DECODE) {
-    threads = V<1>::NT;
-    k = dual ? (packed ? gemm_stream_decode<true, true> : gemm_stream_decode<true, false>)
-             : (packed ? gemm_stream_decode<false, true> : gemm_stream_decode<false, false>);
-  } else {
-    threads = V<0>::NT;
-    k = dual ? (packed ? gemm_stream_prefill<true, true> : gemm_stream_prefill<true, false>)
-             : (packed ? gemm_stream_prefill<false, true> : gemm_stream_prefill<false, false>);
+typedef void (*stream_kernel_t)(StreamArgs);
+
+// The kernel of one variant for an epilogue; the packed layout only with the
+// SwiGLU epilogues (null otherwise).
+template <int VAR>
+static stream_kernel_t pick_kernel(int epi, bool packed) {
+#define MOE_STREAM_K(E, P) (VAR == 0 ? gemm_stream_prefill<E, P> : gemm_stream_decode<E, P>)
+  if (packed) {
+    switch (epi) {
+      case EPI_SILU_GLU: return MOE_STREAM_K(EPI_SILU_GLU, true);
+      case EPI_PLAIN: return MOE_STREAM_K(EPI_PLAIN, true);
+      default: return nullptr;
+    }
   }
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(num_cus())), dim3(threads), 0, s, a);
+  switch (epi) {
+    case EPI_SILU_GLU: return MOE_STREAM_K(EPI_SILU_GLU, false);
+    case EPI_GELU_GLU: return MOE_STREAM_K(EPI_GELU_GLU, false);
+    case EPI_PLAIN: return MOE_STREAM_K(EPI_PLAIN, false);
+    case EPI_BIAS: return MOE_STREAM_K(EPI_BIAS, false);
+    case EPI_BIAS_GELU: return MOE_STREAM_K(EPI_BIAS_GELU, false);
+    default: return nullptr;
+  }
+#undef MOE_STREAM_K
+}
+
+static hipError_t launch_stream(const Plan &p, const StreamArgs &a, int epi, bool packed, hipStream_t s) {
+  const bool decode = p.path == PATH_STREAM_DECODE;
+  const stream_kernel_t k = decode ? pick_kernel<1>(epi, packed) : pick_kernel<0>(epi, packed);
+  if (!k) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(num_cus())), dim3(decode ? V<1>::NT : V<0>::NT), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_stream_gate_up(const Plan &p, const void *u, const void *W1, const void *W3,
-                                 const void *W1s, const void *W3s, const PackedView *pk, hipStream_t s) {
+hipError_t launch_stream_gate_up(const Plan &p, const void *u, const Experts &x, const PackedView *pk,
+                                 hipStream_t s) {
   const moe_cfg &c = p.cfg;
+  const int epi = gate_up_epi(p.kind);
+  const bool dual = epi_dual(epi);
   StreamArgs a = base_args(p, 0);
   a.A_routed = u;
   a.A_shared = u;
   a.gather = 1;
-  a.B0_routed = W1;
-  a.B1_routed = W3;
-  a.B0_shared = W1s;
-  a.B1_shared = W3s;
+  a.B0_routed = x.W1;
+  a.B1_routed = dual ? x.W3 : nullptr;
+  a.B0_shared = x.W1s;
+  a.B1_shared = dual ? x.W3s : nullptr;
   a.Bp_routed = pk ? pk->gu : nullptr;
   a.Bp_shared = pk ? pk->gu_s : nullptr;
+  a.bias_routed = x.b1;
+  a.bias_shared = x.b1s;
   a.N_routed = c.F;
   a.N_shared = c.F_shared;
   a.K_routed = c.d;
   a.K_shared = c.d;
   a.C_routed = p.H;
   a.C_shared = p.Hs;
-  return launch_stream(p, a, true, pk != nullptr, s);
+  return launch_stream(p, a, epi, pk != nullptr, s);
 }
 
-hipError_t launch_stream_down(const Plan &p, const void *W2, const void *W2s, const PackedView *pk,
-                              hipStream_t s) {
+hipError_t launch_stream_down(const Plan &p, const Experts &x, const PackedView *pk, hipStream_t s) {
   const moe_cfg &c = p.cfg;
   StreamArgs a = base_args(p, 1);
   a.A_routed = p.H;
   a.A_shared = p.Hs;
   a.gather = 0;
-  a.B0_routed = W2;
+  a.B0_routed = x.W2;
   a.B1_routed = nullptr;
-  a.B0_shared = W2s;
+  a.B0_shared = x.W2s;
   a.B1_shared = nullptr;
   a.Bp_routed = pk ? pk->dn : nullptr;
   a.Bp_shared = pk ? pk->dn_s : nullptr;
+  a.bias_routed = x.b2;
+  a.bias_shared = x.b2s;
   a.N_routed = c.d;
   a.N_shared = c.d;
   a.K_routed = c.F;
   a.K_shared = c.F_shared;
   a.C_routed = p.O;
   a.C_shared = p.Z;
-  return launch_stream(p, a, false, pk != nullptr, s);
+  return launch_stream(p, a, down_epi(p.kind), pk != nullptr, s);
 }
 
 }  // namespace moe

@@ -1,14 +1,18 @@
 // Stages 3 and 4: the experts, as grouped GEMMs over the tile list.
 //
 // Each expert is SwiGLU, FFN(x) = W2 (SiLU(W1 x) * W3 x) ("Sparse MoE FFN"
-// (DeepSeek-V3), "How it works", expert equation).  "Mixture of experts and
-// architecture families", "The router and load balancing", notes that the
-// per-expert loop is batched as grouped GEMMs; here one launch covers every
-// expert plus the shared expert (an extra group whose rows are all tokens).
+// (DeepSeek-V3), "How it works", expert equation), or one of the other
+// bodies the epilogue selects: GEGLU, or the biased GELU MLP W2 GELU(W1 x +
+// b1) + b2 ("Lesson 2 -- From the Dense FFN to a Layer of Experts", section
+// 2).  "Mixture of experts and architecture families", "The router and load
+// balancing", notes that the per-expert loop is batched as grouped GEMMs;
+// here one launch covers every expert plus the shared expert (an extra group
+// whose rows are all tokens).
 //
-//   gate_up: H[row] = SiLU(x W1^T) * (x W3^T), x = u[token of row]  (gather)
-//   down:    O[row] = H[row] W2^T   (routed rows, bf16 or fp32)
-//            Z[t]   = Hs[t] W2s^T   (shared rows)
+//   gate_up: H[row] = act(x W1^T) * (x W3^T), x = u[token of row]  (gather)
+//            or GELU(x W1^T + b1) for the GELU MLP
+//   down:    O[row] = H[row] W2^T (+ b2)   (routed rows, bf16 or fp32)
+//            Z[t]   = Hs[t] W2s^T (+ b2s)  (shared rows)
 //
 // Both are C = A B^T with A [rows][K] and B [N][K] row-major (K contiguous),
 // the layout in which the weights arrive.  bf16 runs on the gfx950 MFMA
@@ -42,7 +46,18 @@ struct GemmArgs {
   void *C_routed;  // [rows][N]
   void *C_shared;  // [rows][N]
   int c_shared_f32;
+  int epi;                   // Epi
+  const void *bias_routed;   // [E][N] or null (EPI_BIAS, EPI_BIAS_GELU)
+  const void *bias_shared;   // [N] or null
 };
+
+// The bias row of a tile's group, or null.
+__device__ __forceinline__ const void *group_bias(const GemmArgs &g, bool shared, int group, int N, int es) {
+  if (g.epi < EPI_BIAS) return nullptr;
+  if (shared) return g.bias_shared;
+  if (!g.bias_routed) return nullptr;
+  return static_cast<const char *>(g.bias_routed) + static_cast<int64_t>(group) * N * es;
+}
 
 template <bool DUAL>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16(GemmArgs g) {
@@ -171,6 +186,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16(GemmArgs g) {
   if (!wave_rows) return;
   const bool f32_out = shared && g.c_shared_f32;
   void *C = shared ? g.C_shared : g.C_routed;
+  const uint16_t *bias = static_cast<const uint16_t *>(group_bias(g, shared, tl.group, N, 2));
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -181,7 +197,12 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16(GemmArgs g) {
         const int col = n0 + wn * 64 + ni * 32 + (lane & 31);
         if (row >= tl.nrows || col >= N) continue;
         float v = acc[mi][ni][0][r];
-        if (DUAL) v = silu(v) * acc[mi][ni][NM - 1][r];
+        if (DUAL) {
+          v = (g.epi == EPI_GELU_GLU ? gelu(v) : silu(v)) * acc[mi][ni][NM - 1][r];
+        } else {
+          if (bias) v += bf16_to_f32(bias[col]);
+          if (g.epi == EPI_BIAS_GELU) v = gelu(v);
+        }
         const int64_t o = (static_cast<int64_t>(tl.row0) + row) * N + col;
         if (f32_out)
           static_cast<float *>(C)[o] = v;
@@ -262,11 +283,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs g) {
   const int col = n0 + tx;
   if (col >= N) return;
   float *C = static_cast<float *>(shared ? g.C_shared : g.C_routed);
+  const float *bias = static_cast<const float *>(group_bias(g, shared, tl.group, N, 4));
+  const float bcol = bias ? bias[col] : 0.f;
 #pragma unroll
   for (int i = 0; i < FM / 4; ++i) {
     const int row = ty + 4 * i;
     if (row >= tl.nrows) continue;
-    const float v = DUAL ? silu(acc0[i]) * acc1[i] : acc0[i];
+    float v;
+    if (DUAL) {
+      v = (g.epi == EPI_GELU_GLU ? gelu(acc0[i]) : silu(acc0[i])) * acc1[i];
+    } else {
+      v = bias ? acc0[i] + bcol : acc0[i];
+      if (g.epi == EPI_BIAS_GELU) v = gelu(v);
+    }
     C[(static_cast<int64_t>(tl.row0) + row) * N + col] = v;
   }
 }
@@ -293,8 +322,7 @@ hipError_t launch_on(const Plan &p, const GemmArgs &g, bool dual, int n_max, hip
 
 int gemm_tile_m(int dtype) { return dtype == MOE_BF16 ? BM : FM; }
 
-hipError_t launch_gate_up(const Plan &p, const void *u, const void *W1, const void *W3,
-                          const void *W1s, const void *W3s, hipStream_t s) {
+hipError_t launch_gate_up(const Plan &p, const void *u, const Experts &x, hipStream_t s) {
   const moe_cfg &c = p.cfg;
   GemmArgs g{};
   g.tiles = p.tiles;
@@ -305,10 +333,14 @@ hipError_t launch_gate_up(const Plan &p, const void *u, const void *W1, const vo
   g.A_routed = u;
   g.A_shared = u;
   g.gather = 1;
-  g.B0_routed = W1;
-  g.B1_routed = W3;
-  g.B0_shared = W1s;
-  g.B1_shared = W3s;
+  g.epi = gate_up_epi(p.kind);
+  const bool dual = epi_dual(g.epi);
+  g.B0_routed = x.W1;
+  g.B1_routed = dual ? x.W3 : nullptr;
+  g.B0_shared = x.W1s;
+  g.B1_shared = dual ? x.W3s : nullptr;
+  g.bias_routed = x.b1;
+  g.bias_shared = x.b1s;
   g.N_routed = c.F;
   g.N_shared = c.F_shared;
   g.K_routed = c.d;
@@ -317,10 +349,10 @@ hipError_t launch_gate_up(const Plan &p, const void *u, const void *W1, const vo
   g.C_shared = p.Hs;
   g.c_shared_f32 = 0;
   const int n_max = c.F > c.F_shared ? c.F : c.F_shared;
-  return launch_on(p, g, true, n_max, s);
+  return launch_on(p, g, dual, n_max, s);
 }
 
-hipError_t launch_down(const Plan &p, const void *W2, const void *W2s, hipStream_t s) {
+hipError_t launch_down(const Plan &p, const Experts &x, hipStream_t s) {
   const moe_cfg &c = p.cfg;
   GemmArgs g{};
   g.tiles = p.tiles;
@@ -331,10 +363,13 @@ hipError_t launch_down(const Plan &p, const void *W2, const void *W2s, hipStream
   g.A_routed = p.H;
   g.A_shared = p.Hs;
   g.gather = 0;
-  g.B0_routed = W2;
+  g.epi = down_epi(p.kind);
+  g.B0_routed = x.W2;
   g.B1_routed = nullptr;
-  g.B0_shared = W2s;
+  g.B0_shared = x.W2s;
   g.B1_shared = nullptr;
+  g.bias_routed = x.b2;
+  g.bias_shared = x.b2s;
   g.N_routed = c.d;
   g.N_shared = c.d;
   g.K_routed = c.F;

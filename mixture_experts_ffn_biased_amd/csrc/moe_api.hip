@@ -39,13 +39,15 @@ moe_status validate(const moe_cfg *c) {
 static size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // The streaming kernels need bf16 and whole 256-row weight slabs
-// (d % 256, F % 128, F_shared % 128).  With at least 64 routed rows per
-// expert on average they run 256-row tiles (prefill); with fewer, 32-row
-// tiles with a deeper weight ring (decode), which also needs F % 256 and
-// F_shared % 256.  Everything else takes the tiled kernels.
-static int choose_path(const moe_cfg &c) {
+// (d % 256, F % 128, F_shared % 128; the GELU MLP's single gate_up product
+// F % 256, F_shared % 256).  With at least 64 routed rows per expert on
+// average they run 256-row tiles (prefill); with fewer, 32-row tiles with a
+// deeper weight ring (decode), which also needs F % 256 and F_shared % 256.
+// Everything else takes the tiled kernels.
+static int choose_path(const moe_cfg &c, int kind) {
   if (c.dtype != MOE_BF16) return PATH_TILED;
   if (c.d % 256 != 0 || c.F % 128 != 0 || c.F_shared % 128 != 0) return PATH_TILED;
+  if (kind == MOE_EXPERT_GELU_MLP && (c.F % 256 != 0 || c.F_shared % 256 != 0)) return PATH_TILED;
   const int64_t S = c.T * c.k;
   int path = PATH_STREAM;
   if (S < 64LL * c.E) {
@@ -63,10 +65,15 @@ static bool packable(const moe_cfg &c) {
   return c.dtype == MOE_BF16 && c.d % 256 == 0 && c.F % 256 == 0 && c.F_shared % 256 == 0;
 }
 
-void make_plan(const moe_cfg &c, void *base, Plan *p) {
+static bool valid_kind(int kind) {
+  return kind == MOE_EXPERT_SWIGLU || kind == MOE_EXPERT_GEGLU || kind == MOE_EXPERT_GELU_MLP;
+}
+
+void make_plan(const moe_cfg &c, int kind, void *base, Plan *p) {
   p->cfg = c;
+  p->kind = kind;
   p->S = c.T * c.k;
-  p->path = choose_path(c);
+  p->path = choose_path(c, kind);
   p->tile_m = p->path == PATH_TILED ? gemm_tile_m(c.dtype) : stream_tile_m(p->path);
   p->tile_balanced = p->path == PATH_TILED ? 0 : stream_tile_balanced(p->path);
   p->router_splits = (c.dtype == MOE_BF16 && c.d % 128 == 0) ? router_splits(c.T, c.d) : 1;
@@ -93,7 +100,7 @@ void make_plan(const moe_cfg &c, void *base, Plan *p) {
   p->tile_count = static_cast<int32_t *>(take(sizeof(int32_t)));
   p->max_items_gu = p->max_items_dn = 0;
   if (p->path != PATH_TILED) {
-    const int64_t nslab = stream_nslab_gate_up(c.F > c.F_shared ? c.F : c.F_shared);
+    const int64_t nslab = stream_nslab_gate_up(c.F > c.F_shared ? c.F : c.F_shared, kind);
     p->max_items_gu = p->max_tiles * nslab;
     p->max_items_dn = p->max_tiles * stream_nslab_down(c.d);
   }
@@ -127,20 +134,27 @@ using namespace moe;
 
 extern "C" {
 
-size_t moe_workspace_bytes(const moe_cfg *cfg) {
-  if (validate(cfg) != MOE_OK) return 0;
+size_t moe_workspace_bytes(const moe_cfg *cfg) { return moe_workspace_bytes_ex(cfg, MOE_EXPERT_SWIGLU); }
+
+size_t moe_workspace_bytes_ex(const moe_cfg *cfg, int32_t kind) {
+  if (validate(cfg) != MOE_OK || !valid_kind(kind)) return 0;
   Plan p;
-  make_plan(*cfg, nullptr, &p);
+  make_plan(*cfg, kind, nullptr, &p);
   return p.bytes;
 }
 
 moe_status moe_check_cfg(const moe_cfg *cfg) { return validate(cfg); }
 
 moe_status moe_plan_describe(const moe_cfg *cfg, int32_t *gemm_path, int32_t *tile_rows) {
+  return moe_plan_describe_ex(cfg, MOE_EXPERT_SWIGLU, gemm_path, tile_rows);
+}
+
+moe_status moe_plan_describe_ex(const moe_cfg *cfg, int32_t kind, int32_t *gemm_path, int32_t *tile_rows) {
   const moe_status st = validate(cfg);
   if (st != MOE_OK) return st;
+  if (!valid_kind(kind)) return MOE_ERR_DTYPE;
   Plan p;
-  make_plan(*cfg, nullptr, &p);
+  make_plan(*cfg, kind, nullptr, &p);
   if (gemm_path) *gemm_path = p.path;
   if (tile_rows) *tile_rows = p.tile_m;
   return MOE_OK;
@@ -160,18 +174,18 @@ const char *moe_status_str(int status) {
   }
 }
 
-static moe_status prepare(const moe_cfg *cfg, void *workspace, size_t workspace_bytes, Plan *p) {
+static moe_status prepare(const moe_cfg *cfg, int kind, void *workspace, size_t workspace_bytes, Plan *p) {
   Plan probe;
-  make_plan(*cfg, nullptr, &probe);
+  make_plan(*cfg, kind, nullptr, &probe);
   if (!workspace) return MOE_ERR_WORKSPACE;
   if (workspace_bytes < probe.bytes) return MOE_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MOE_ERR_ALIGN;
-  make_plan(*cfg, workspace, p);
+  make_plan(*cfg, kind, workspace, p);
   return MOE_OK;
 }
 
 // Validation shared by the two forward entry points; *p is filled on success.
-static moe_status check_forward(const void *u, const void *W_router, const moe_cfg *cfg, const void *y,
+static moe_status check_forward(const void *u, const void *W_router, const moe_cfg *cfg, int kind, const void *y,
                                 const int32_t *topk_idx, const float *gates, void *workspace,
                                 size_t workspace_bytes, Plan *p) {
   if (!u || !W_router || !y || !topk_idx || !gates) return MOE_ERR_NULL;
@@ -180,13 +194,28 @@ static moe_status check_forward(const void *u, const void *W_router, const moe_c
   const char *a = static_cast<const char *>(u);
   const char *b = static_cast<const char *>(y);
   if (a < b + bytes && b < a + bytes) return MOE_ERR_SHAPE;  // y aliases u
-  return prepare(cfg, workspace, workspace_bytes, p);
+  return prepare(cfg, kind, workspace, workspace_bytes, p);
+}
+
+// The SwiGLU experts of the plain entry points (shared may be null).
+static Experts swiglu_experts(const void *W1, const void *W3, const void *W2, const moe_shared *shared) {
+  Experts x{};
+  x.kind = MOE_EXPERT_SWIGLU;
+  x.W1 = W1;
+  x.W3 = W3;
+  x.W2 = W2;
+  if (shared) {
+    x.W1s = shared->W1;
+    x.W3s = shared->W3;
+    x.W2s = shared->W2;
+  }
+  return x;
 }
 
 // residual: nullptr for the layer, the block input h for the block form.
+// pk: the packed buffer's regions (SwiGLU), or null for x's plain weights.
 static moe_status run_layer(const Plan &p, const void *u, const void *W_router, const float *bias,
-                            const void *W1, const void *W3, const void *W2, const moe_shared *shared,
-                            const PackedView *pk, void *y, int32_t *topk_idx, float *gates,
+                            const Experts &x, const PackedView *pk, void *y, int32_t *topk_idx, float *gates,
                             hipStream_t s, const void *residual = nullptr) {
   (void)hipGetLastError();  // report only errors of the launches below
   Record rec{};
@@ -216,18 +245,15 @@ static moe_status run_layer(const Plan &p, const void *u, const void *W_router, 
     }
     return MOE_ERR_HIP;
   };
-  const void *W1s = shared ? shared->W1 : nullptr, *W3s = shared ? shared->W3 : nullptr;
-  const void *W2s = shared ? shared->W2 : nullptr;
   mark(0);
   if (launch_router_topk(p, u, W_router, bias, topk_idx, gates, s) != hipSuccess) return fail();
   mark(1);
   if (launch_permute(p, topk_idx, s) != hipSuccess) return fail();
   mark(2);
-  hipError_t err = p.path == PATH_TILED ? launch_gate_up(p, u, W1, W3, W1s, W3s, s)
-                                        : launch_stream_gate_up(p, u, W1, W3, W1s, W3s, pk, s);
+  hipError_t err = p.path == PATH_TILED ? launch_gate_up(p, u, x, s) : launch_stream_gate_up(p, u, x, pk, s);
   if (err != hipSuccess) return fail();
   mark(3);
-  err = p.path == PATH_TILED ? launch_down(p, W2, W2s, s) : launch_stream_down(p, W2, W2s, pk, s);
+  err = p.path == PATH_TILED ? launch_down(p, x, s) : launch_stream_down(p, x, pk, s);
   if (err != hipSuccess) return fail();
   mark(4);
   if (launch_combine(p, gates, residual, y, s) != hipSuccess) return fail();
@@ -254,10 +280,49 @@ moe_status moe_layer_forward(const void *u, const void *W_router, const float *b
   for (const void *q : ptrs)
     if (!aligned16(q)) return MOE_ERR_ALIGN;
   Plan p;
-  st = check_forward(u, W_router, cfg, y, topk_idx, gates, workspace, workspace_bytes, &p);
+  st = check_forward(u, W_router, cfg, MOE_EXPERT_SWIGLU, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
-  return run_layer(p, u, W_router, bias, W1, W3, W2, shared, nullptr, y, topk_idx, gates,
+  return run_layer(p, u, W_router, bias, swiglu_experts(W1, W3, W2, shared), nullptr, y, topk_idx, gates,
                    static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_layer_forward_ex(const void *u, const void *W_router, const float *bias,
+                                const moe_experts *experts, const moe_cfg *cfg, void *y, int32_t *topk_idx,
+                                float *gates, void *workspace, size_t workspace_bytes, void *stream) {
+  moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if (!experts) return MOE_ERR_NULL;
+  const moe_experts &e = *experts;
+  if (!valid_kind(e.kind)) return MOE_ERR_DTYPE;
+  const bool gated = e.kind != MOE_EXPERT_GELU_MLP;
+  const bool has_shared = e.W1s || e.W3s || e.W2s;
+  if ((cfg->F_shared > 0) != has_shared) return MOE_ERR_CFG;
+  if (gated && (e.b1 || e.b2 || e.b1s || e.b2s)) return MOE_ERR_CFG;
+  if (!has_shared && (e.b1s || e.b2s)) return MOE_ERR_CFG;
+  if (cfg->T == 0) return MOE_OK;
+  if (!e.W1 || !e.W2 || (gated && !e.W3)) return MOE_ERR_NULL;
+  if (has_shared && (!e.W1s || !e.W2s || (gated && !e.W3s))) return MOE_ERR_NULL;
+  const void *ptrs[] = {e.W1, e.W2, e.W3, e.b1, e.b2, e.W1s, e.W2s, e.W3s, e.b1s, e.b2s};
+  for (const void *q : ptrs)
+    if (q && !aligned16(q)) return MOE_ERR_ALIGN;
+  Plan p;
+  st = check_forward(u, W_router, cfg, e.kind, y, topk_idx, gates, workspace, workspace_bytes, &p);
+  if (st != MOE_OK) return st;
+  Experts x{};
+  x.kind = e.kind;
+  x.W1 = e.W1;
+  x.W3 = gated ? e.W3 : nullptr;
+  x.W2 = e.W2;
+  x.b1 = e.b1;
+  x.b2 = e.b2;
+  if (has_shared) {
+    x.W1s = e.W1s;
+    x.W3s = gated ? e.W3s : nullptr;
+    x.W2s = e.W2s;
+    x.b1s = e.b1s;
+    x.b2s = e.b2s;
+  }
+  return run_layer(p, u, W_router, bias, x, nullptr, y, topk_idx, gates, static_cast<hipStream_t>(stream));
 }
 
 size_t moe_packed_weights_bytes(const moe_cfg *cfg) {
@@ -297,14 +362,13 @@ moe_status moe_layer_forward_packed(const void *u, const void *W_router, const f
   if (!packed) return MOE_ERR_NULL;
   if (!aligned16(packed)) return MOE_ERR_ALIGN;
   Plan p;
-  st = check_forward(u, W_router, cfg, y, topk_idx, gates, workspace, workspace_bytes, &p);
+  st = check_forward(u, W_router, cfg, MOE_EXPERT_SWIGLU, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
   if (p.path == PATH_TILED) return MOE_ERR_SHAPE;  // too many tiles for the streaming schedule
   const PackedView pk = packed_view(*cfg, packed);
-  // The shared expert is present iff F_shared > 0; its pointers come from pk.
-  moe_shared sh{pk.gu_s, pk.gu_s, pk.dn_s};
-  return run_layer(p, u, W_router, bias, nullptr, nullptr, nullptr, cfg->F_shared > 0 ? &sh : nullptr,
-                   &pk, y, topk_idx, gates, static_cast<hipStream_t>(stream));
+  // The shared expert is present iff F_shared > 0 (the kernels read pk).
+  return run_layer(p, u, W_router, bias, swiglu_experts(nullptr, nullptr, nullptr, nullptr), &pk, y, topk_idx,
+                   gates, static_cast<hipStream_t>(stream));
 }
 
 // ---- pre-norm residual block ----------------------------------------------
@@ -314,7 +378,7 @@ static size_t elem_bytes(const moe_cfg &c) { return c.dtype == MOE_BF16 ? 2 : 4;
 size_t moe_block_workspace_bytes(const moe_cfg *cfg) {
   if (validate(cfg) != MOE_OK || cfg->d > rmsnorm_max_d()) return 0;
   Plan p;
-  make_plan(*cfg, nullptr, &p);
+  make_plan(*cfg, MOE_EXPERT_SWIGLU, nullptr, &p);
   return p.bytes + align_up(static_cast<size_t>(cfg->T) * cfg->d * elem_bytes(*cfg));
 }
 
@@ -360,7 +424,7 @@ moe_status moe_block_forward(const void *h, const void *norm_weight, float norm_
   for (const void *q : ptrs)
     if (!aligned16(q)) return MOE_ERR_ALIGN;
   Plan p;
-  st = check_forward(h, W_router, cfg, y, topk_idx, gates, workspace, workspace_bytes, &p);
+  st = check_forward(h, W_router, cfg, MOE_EXPERT_SWIGLU, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
   void *un = nullptr;
   st = block_setup(norm_weight, norm_eps, cfg, p, workspace, workspace_bytes, &un);
@@ -369,7 +433,7 @@ moe_status moe_block_forward(const void *h, const void *norm_weight, float norm_
   (void)hipGetLastError();
   if (launch_rmsnorm(h, norm_weight, norm_eps, cfg->T, cfg->d, cfg->dtype, un, s) != hipSuccess)
     return MOE_ERR_HIP;
-  return run_layer(p, un, W_router, bias, W1, W3, W2, shared, nullptr, y, topk_idx, gates, s, h);
+  return run_layer(p, un, W_router, bias, swiglu_experts(W1, W3, W2, shared), nullptr, y, topk_idx, gates, s, h);
 }
 
 moe_status moe_block_forward_packed(const void *h, const void *norm_weight, float norm_eps, const void *W_router,
@@ -383,7 +447,7 @@ moe_status moe_block_forward_packed(const void *h, const void *norm_weight, floa
   if (!packed) return MOE_ERR_NULL;
   if (!aligned16(packed)) return MOE_ERR_ALIGN;
   Plan p;
-  st = check_forward(h, W_router, cfg, y, topk_idx, gates, workspace, workspace_bytes, &p);
+  st = check_forward(h, W_router, cfg, MOE_EXPERT_SWIGLU, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
   if (p.path == PATH_TILED) return MOE_ERR_SHAPE;
   void *un = nullptr;
@@ -394,9 +458,8 @@ moe_status moe_block_forward_packed(const void *h, const void *norm_weight, floa
   if (launch_rmsnorm(h, norm_weight, norm_eps, cfg->T, cfg->d, cfg->dtype, un, s) != hipSuccess)
     return MOE_ERR_HIP;
   const PackedView pk = packed_view(*cfg, packed);
-  moe_shared sh{pk.gu_s, pk.gu_s, pk.dn_s};
-  return run_layer(p, un, W_router, bias, nullptr, nullptr, nullptr, cfg->F_shared > 0 ? &sh : nullptr, &pk, y,
-                   topk_idx, gates, s, h);
+  return run_layer(p, un, W_router, bias, swiglu_experts(nullptr, nullptr, nullptr, nullptr), &pk, y, topk_idx,
+                   gates, s, h);
 }
 
 moe_status moe_balance_update(const int32_t *topk_idx, int64_t T, int32_t k, int32_t E, float gamma,
@@ -424,7 +487,7 @@ moe_status moe_route_debug(const void *u, const void *W_router, const float *bia
   if (!u || !W_router || !topk_idx || !gates) return MOE_ERR_NULL;
   if (!aligned16(u) || !aligned16(W_router)) return MOE_ERR_ALIGN;
   Plan p;
-  st = prepare(cfg, workspace, workspace_bytes, &p);
+  st = prepare(cfg, MOE_EXPERT_SWIGLU, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();

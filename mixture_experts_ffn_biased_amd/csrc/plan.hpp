@@ -48,6 +48,31 @@ enum GemmPath {
   PATH_STREAM_DECODE = 2,  // gemm_stream.hip decode variant: 32-row tiles, deep weight ring
 };
 
+// Expert weights of one call in the plain layout and the body they form
+// (moe_expert_kind).  W3 / W3s are unused by the GELU MLP; b1, b2, b1s, b2s
+// are its biases in the layer dtype (null: zero) and null for the gated kinds.
+struct Experts {
+  int kind;
+  const void *W1, *W3, *W2, *b1, *b2;
+  const void *W1s, *W3s, *W2s, *b1s, *b2s;
+};
+
+// Epilogue of a grouped-GEMM tile.  The gated gate_up products hold two
+// accumulators (W1 and W3 rows); the others one, plus an optional bias row
+// of the group ([N] in the layer dtype, null: zero).
+enum Epi {
+  EPI_SILU_GLU = 0,   // SiLU(a1) * a3
+  EPI_GELU_GLU = 1,   // GELU(a1) * a3
+  EPI_PLAIN = 2,      // a
+  EPI_BIAS = 3,       // a + bias[col]
+  EPI_BIAS_GELU = 4,  // GELU(a + bias[col])
+};
+__host__ __device__ constexpr bool epi_dual(int epi) { return epi <= EPI_GELU_GLU; }
+inline int gate_up_epi(int kind) {
+  return kind == MOE_EXPERT_GELU_MLP ? EPI_BIAS_GELU : (kind == MOE_EXPERT_GEGLU ? EPI_GELU_GLU : EPI_SILU_GLU);
+}
+inline int down_epi(int kind) { return kind == MOE_EXPERT_GELU_MLP ? EPI_BIAS : EPI_PLAIN; }
+
 // Device views of the four regions of a packed weight buffer.
 struct PackedView {
   const void *gu;    // routed W1/W3 stage blocks
@@ -58,6 +83,7 @@ struct PackedView {
 
 struct Plan {
   moe_cfg cfg;
+  int kind;         // moe_expert_kind
   int path;         // GemmPath
   int64_t S;        // routed slots, T*k
   int tile_m;       // rows per grouped-GEMM tile (at most)
@@ -79,7 +105,7 @@ struct Plan {
   int2 *items_dn;       //              and of the down GEMM
   int32_t *sched_meta;  //              [2][3][8] list offsets, lengths, counters
   int64_t max_items_gu, max_items_dn;
-  void *H;              // [S][F]        SiLU(W1 x) * W3 x of each routed slot
+  void *H;              // [S][F]        hidden activations of each routed slot
   void *Hs;             // [T][F_shared] same for the shared expert
   void *O;              // [S][d]        expert output of each routed slot
   void *Z;              // [T][d]        shared expert output (layer dtype)
@@ -88,15 +114,14 @@ struct Plan {
 
 moe_status validate(const moe_cfg *c);
 int router_splits(int64_t T, int d);
-// Fills *p; base == nullptr computes only the size.
-void make_plan(const moe_cfg &c, void *base, Plan *p);
+// Fills *p for experts of the given kind; base == nullptr computes only the size.
+void make_plan(const moe_cfg &c, int kind, void *base, Plan *p);
 
 hipError_t launch_router_topk(const Plan &p, const void *u, const void *Wr, const float *bias,
                               int32_t *topk_idx, float *gates, hipStream_t s);
 hipError_t launch_permute(const Plan &p, const int32_t *topk_idx, hipStream_t s);
-hipError_t launch_gate_up(const Plan &p, const void *u, const void *W1, const void *W3,
-                          const void *W1s, const void *W3s, hipStream_t s);
-hipError_t launch_down(const Plan &p, const void *W2, const void *W2s, hipStream_t s);
+hipError_t launch_gate_up(const Plan &p, const void *u, const Experts &x, hipStream_t s);
+hipError_t launch_down(const Plan &p, const Experts &x, hipStream_t s);
 // residual: optional [T][d] in the layer dtype, added to y last (the block form).
 hipError_t launch_combine(const Plan &p, const float *gates, const void *residual, void *y, hipStream_t s);
 int rmsnorm_max_d();
@@ -106,7 +131,7 @@ hipError_t launch_rmsnorm(const void *h, const void *g, float eps, int64_t T, in
 int stream_tile_m(int path);
 int stream_max_chunks();
 int stream_tile_balanced(int path);
-int stream_nslab_gate_up(int F);
+int stream_nslab_gate_up(int F, int kind);
 int stream_nslab_down(int d);
 size_t packed_weights_bytes(const moe_cfg &c);
 PackedView packed_view(const moe_cfg &c, const void *base);
@@ -114,10 +139,10 @@ hipError_t launch_pack_weights(const moe_cfg &c, const void *W1, const void *W3,
                                const void *W1s, const void *W3s, const void *W2s, void *packed,
                                hipStream_t s);
 hipError_t launch_stream_schedule(const Plan &p, hipStream_t s);
-// pk == nullptr: plain weight layout; else the packed buffer's regions.
-hipError_t launch_stream_gate_up(const Plan &p, const void *u, const void *W1, const void *W3,
-                                 const void *W1s, const void *W3s, const PackedView *pk, hipStream_t s);
-hipError_t launch_stream_down(const Plan &p, const void *W2, const void *W2s, const PackedView *pk,
-                              hipStream_t s);
+// pk == nullptr: the plain weights of x; else the packed buffer's regions
+// (SwiGLU only) and x's pointers are not read.
+hipError_t launch_stream_gate_up(const Plan &p, const void *u, const Experts &x, const PackedView *pk,
+                                 hipStream_t s);
+hipError_t launch_stream_down(const Plan &p, const Experts &x, const PackedView *pk, hipStream_t s);
 
 }  // namespace moe

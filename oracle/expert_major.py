@@ -13,7 +13,8 @@ softmax over that subset, so the two oracles must agree.
 The expert loop is the same page's masked loop: for each expert, take the rows
 whose selection contains it, run the expert on those rows, weight and add.
 Experts are SwiGLU ("Sparse MoE FFN" (DeepSeek-V3), "How it works"):
-W2 (SiLU(W1 x) * W3 x); or GEGLU, GELU in place of SiLU; or the biased GELU
+W2 (SiLU(W1 x) * W3 x); or GEGLU, GELU in place of SiLU (named beside SwiGLU
+in the cheat sheet's "Calculator defaults"); or the biased GELU
 MLP of "Lesson 2 -- From the Dense FFN to a Layer of Experts", section 2:
 W2 GELU(W1 x + b1) + b2, with GELU(x) = x Phi(x) (SciPy's erf here).
 """

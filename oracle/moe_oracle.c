@@ -27,7 +27,8 @@
  *       ["Sparse MoE FFN", "How it works", expert equation]; the generic
  *       expert of "Lesson 2 -- From the Dense FFN to a Layer of Experts",
  *       section 2, W2 phi(W1 u + b1) + b2 with phi = GELU, and the gated unit
- *       with GELU in place of SiLU (GEGLU) are the other two bodies
+ *       with GELU in place of SiLU (GEGLU, named beside SwiGLU in the cheat
+ *       sheet's "Calculator defaults") are the other two bodies
  *       (oracle_forward_ex); GELU(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2
  *       ["Sparse MoE FFN", "How it works", expert equation]
  *   - y = sum_j g_j FFN_{i_j}(u) + FFN_shared(u), no residual, no dropping

@@ -20,6 +20,9 @@ Recipe (every tensor):
     0 replaced by ``expert0_scale`` * m when the caller passes that scale.
   * block form: u is the block input h; the RMSNorm weight is 1 + 0.1 N(0, 1)
     (``make_norm_weight``, tensor id 10).
+  * biased GELU-MLP experts (``make_ffn_biases``): b1 ~ 0.5 N(0, 1) [E][F],
+    b2 ~ 0.1 N(0, 1) [E][d], b1s, b2s likewise for the shared expert (tensor
+    ids 11-14), in the workload's dtype.
 
 The same (workload, seed, device) always gives the same tensors.  Draws on
 "cpu" and on "cuda" differ from each other; each test states which it uses.
@@ -33,7 +36,8 @@ from typing import Optional
 import torch
 
 TENSOR_IDS = {"u": 0, "W_router": 1, "W1": 2, "W3": 3, "W2": 4, "W1s": 5, "W3s": 6,
-              "W2s": 7, "bias": 8, "skew_dir": 9, "norm_weight": 10}
+              "W2s": 7, "bias": 8, "skew_dir": 9, "norm_weight": 10, "b1": 11, "b2": 12,
+              "b1s": 13, "b2s": 14}
 
 
 @dataclass(frozen=True)
@@ -124,6 +128,20 @@ def make_norm_weight(w: Workload, seed: int = 0, device="cpu") -> torch.Tensor:
     dev = torch.device(device)
     g = 1.0 + _randn((w.d,), _gen(seed, "norm_weight", dev), dev, 0.1, torch.float32)
     return g.to(torch_dtype(w))
+
+
+def make_ffn_biases(w: Workload, seed: int = 0, device="cpu") -> dict:
+    """Additive biases of the GELU-MLP expert body: b1 [E][F], b2 [E][d], and
+    b1s [Fs], b2s [d] when the layer has a shared expert (else None)."""
+    dev = torch.device(device)
+    dt = torch_dtype(w)
+    out = {"b1": _randn((w.E, w.F), _gen(seed, "b1", dev), dev, 0.5, dt),
+           "b2": _randn((w.E, w.d), _gen(seed, "b2", dev), dev, 0.1, dt),
+           "b1s": None, "b2s": None}
+    if w.Fs > 0:
+        out["b1s"] = _randn((w.Fs,), _gen(seed, "b1s", dev), dev, 0.5, dt)
+        out["b2s"] = _randn((w.d,), _gen(seed, "b2s", dev), dev, 0.1, dt)
+    return out
 
 
 def make_u(w: Workload, seed: int = 0, device="cpu") -> torch.Tensor:

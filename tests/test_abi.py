@@ -43,14 +43,18 @@ def test_struct_layout_matches_header(tmp_path):
         '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
         "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(moe_cfg),"
         " offsetof(moe_cfg, d), offsetof(moe_cfg, dtype), offsetof(moe_cfg, n_groups),"
-        " offsetof(moe_cfg, route_scale), sizeof(moe_shared)); return 0;}\n")
+        " offsetof(moe_cfg, route_scale), sizeof(moe_shared));"
+        " printf(\"%zu %zu %zu\\n\", sizeof(moe_experts), offsetof(moe_experts, W1),"
+        " offsetof(moe_experts, b2s)); return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
                                           check=True).stdout.split()]
     c = binding.moe_cfg
+    x = binding.moe_experts
     assert got == [ctypes.sizeof(c), c.d.offset, c.dtype.offset, c.n_groups.offset,
-                   c.route_scale.offset, ctypes.sizeof(binding.moe_shared)]
+                   c.route_scale.offset, ctypes.sizeof(binding.moe_shared),
+                   ctypes.sizeof(x), x.W1.offset, x.b2s.offset]
 
 
 def cfg(**kw):
@@ -190,3 +194,46 @@ def test_block_and_rmsnorm_arguments_are_checked_before_any_launch():
     x = c.to_c()
     assert L.moe_block_forward_packed(p["h"], p["g"], ctypes.c_float(1e-6), p["Wr"], None, None,
                                       ctypes.byref(x), p["y"], p["idx"], p["gates"], p["ws"], blk, None) == -2
+
+
+def test_expert_body_arguments_are_checked_before_any_launch():
+    L = moe.lib()
+    f = ctypes.c_void_p
+    c = cfg(n_groups=1, topk_groups=1)
+    sw = moe.moe_workspace_bytes(c)
+    assert moe.moe_workspace_bytes_ex(c, "swiglu") == sw
+    assert moe.moe_workspace_bytes_ex(c, "geglu") == sw
+    assert moe.moe_workspace_bytes_ex(c, "gelu_mlp") > 0
+    assert moe.moe_workspace_bytes_ex(c, 3) == 0 and moe.moe_workspace_bytes_ex(cfg(E=0), "geglu") == 0
+    p = {n: f(0x10000 * (i + 1)) for i, n in enumerate(
+        ["u", "Wr", "W1", "W3", "W2", "b1", "b2", "W1s", "W3s", "W2s", "b1s", "b2s", "y", "idx", "gates", "ws"])}
+
+    def call(kind=moe.binding.MOE_EXPERT_GELU_MLP, cc=c, ws_bytes=1 << 30, **over):
+        q = dict(p)
+        q.update(over)
+        shared = cc.F_shared > 0
+        ex = binding.moe_experts(kind, q["W1"], q["W3"], q["W2"], q["b1"], q["b2"],
+                                 q["W1s"] if shared else None, q["W3s"] if shared else None,
+                                 q["W2s"] if shared else None, q["b1s"] if shared else None,
+                                 q["b2s"] if shared else None)
+        x = cc.to_c()
+        return L.moe_layer_forward_ex(q["u"], q["Wr"], None, ctypes.byref(ex), ctypes.byref(x), q["y"],
+                                      q["idx"], q["gates"], q["ws"], ws_bytes, None)
+    assert call(kind=5) == -4
+    assert call(kind=moe.binding.MOE_EXPERT_GEGLU) == -3          # biases with a gated body
+    assert call(kind=moe.binding.MOE_EXPERT_GEGLU, b1=None, b2=None, W3=None) == -1
+    assert call(W1=None) == -1 and call(W2=None) == -1
+    assert call(b1=f(0x60008)) == -7
+    assert call(ws_bytes=16) == -5
+    assert call(cc=cfg(n_groups=1, topk_groups=1, T=0)) == 0    # no-op
+    assert call(cc=cfg(n_groups=1, topk_groups=1, F_shared=128), W2s=None) == -1
+    x = c.to_c()
+    assert L.moe_layer_forward_ex(p["u"], p["Wr"], None, None, ctypes.byref(x), p["y"], p["idx"], p["gates"],
+                                  p["ws"], 1 << 30, None) == -1
+    # the GELU MLP's single gate/up product needs whole 256-row slabs for the streaming kernels
+    big = cfg(T=4096, d=256, E=8, k=2, F=384, n_groups=1, topk_groups=1)
+    assert moe.moe_plan_describe_ex(big, "swiglu")[0] == "stream"
+    assert moe.moe_plan_describe_ex(big, "gelu_mlp")[0] == "tiled"
+    assert moe.moe_plan_describe_ex(cfg(T=4096, d=256, E=8, k=2, F=512, n_groups=1, topk_groups=1),
+                                    "gelu_mlp")[0] == "stream"
+    assert moe.moe_plan_describe_ex(big, "geglu") == moe.moe_plan_describe(big)
