@@ -198,7 +198,10 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   const int K = shared ? g.K_shared : g.K_routed;
   const int KT = K / SBK;
   const int n0 = item.y * (DUAL ? SBN / 2 : SBN);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // Wave-uniform by construction; readfirstlane lets the compiler keep it and
+  // every LDS slot address derived from it in SGPRs (the DMA's M0 operand).
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = VAR == 0 ? wave >> 2 : 0, wn = VAR == 0 ? (wave & 3) : wave;
 
   const uint16_t *A = static_cast<const uint16_t *>(shared ? g.A_shared : g.A_routed);
@@ -349,15 +352,20 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
         }
     }
     __syncthreads();
-#pragma unroll 4
-    for (int j = 0; j < BM * 32 / NT; ++j) {
-      const int q = tid + NT * j;
-      const int row = q >> 5, ch = q & 31;
-      const unsigned char *slot =
-          row < 128 ? (row < 64 ? ring.s[0] : ring.s[1]) : (row < 192 ? ring.s[2] : ring.s[3]);
-      if (row < tl.nrows)
-        *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
-            *reinterpret_cast<const uint4 *>(slot + (row & 63) * 512 + ch * 16);
+    // Copy-out slot by slot (static slot index: a runtime choice among the
+    // ring pointers would make the compiler keep them in memory).
+    constexpr int RPS = BM < 64 ? BM : 64;  // rows staged in one slot
+    constexpr int RPP = NT / 32;            // rows per pass, 32 threads of 16 B a row
+#pragma unroll
+    for (int sl = 0; sl < BM / RPS; ++sl) {
+#pragma unroll
+      for (int j = 0; j < RPS / RPP; ++j) {
+        const int rl = j * RPP + (tid >> 5), ch = tid & 31;
+        const int row = sl * RPS + rl;
+        if (row < tl.nrows)
+          *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
+              *reinterpret_cast<const uint4 *>(ring.s[sl] + rl * 512 + ch * 16);
+      }
     }
     __syncthreads();
   }
