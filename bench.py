@@ -16,7 +16,10 @@ Printed: one JSON line with tokens/s, the layer's TFLOP/s and fraction of the
 bf16 MFMA peak, the roofline of the dominant kernel (gate/up, from HIP events
 recorded by the library on the launch stream during the timed steps), the
 decode-shaped layer (T=64, same weights) with its HBM bandwidth, and the CPU
-oracle timed on a bounded sample of the same workload.
+oracle timed on a bounded sample of the same workload.  Informational extras
+(``other_configs``): the Mixtral-shaped layer, the skewed layer without and
+with the balance-loop bias, and one expert-parallel shard's share of the
+DeepSeek-V3 layer.
 """
 import argparse
 import hashlib
@@ -52,6 +55,8 @@ def parse():
                     help="time the plain weight layout instead of the packed one")
     ap.add_argument("--no-plain", action="store_true",
                     help="skip the reference timing of the plain weight layout")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the informational timings of the other layer shapes")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB three times (a plain "
                          "copy kernel of known size, to scale hardware byte counters)")
@@ -157,6 +162,97 @@ def run_layer(w, inp, u, steps, warmup, torch, packed=None):
 
     ms, wall, stage_ms, calls = timed_steps(step, steps, warmup, torch)
     return ms, wall, stage_ms, idx
+
+
+def layer_record(w, ms, stage_ms, hit, path):
+    """Throughput fields of one timed layer shape."""
+    import mixture_experts_ffn_biased_amd as moe
+    tf = w.flops / (ms * 1e-3) / 1e12
+    s = 2 if w.dtype == "bf16" else 4
+    nbytes = (w.E * w.d * s + 4 * w.E + hit * 3 * w.d * w.F * s + 3 * w.d * w.Fs * s + 2 * w.T * w.d * s
+              + 8 * w.T * w.k)
+    return {"T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F, "F_shared": w.Fs, "score_fn": w.score_fn,
+            "gemm_path": path, "ms_per_step": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+            "layer_tflops": round(tf, 2), "layer_mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "experts_hit": hit, "layer_bytes": int(nbytes),
+            "flop_per_byte": round(w.flops / nbytes, 1),
+            "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, stage_ms)}}
+
+
+def time_shape(w, inp, steps, warmup, torch, bias=None):
+    """Pack the shape's weights, time the packed layer, free the weights' copy."""
+    import mixture_experts_ffn_biased_amd as moe
+    cfg = moe.MoeConfig.from_workload(w)
+    packed = moe.moe_pack_weights(inp["W1"], inp["W3"], inp["W2"], inp["shared"], cfg=cfg)
+    if bias is not None:
+        inp = dict(inp, bias=bias)
+    ms, _, stage_ms, idx = run_layer(w, inp, inp["u"], steps, warmup, torch, packed)
+    hit = int(torch.unique(idx).numel())
+    del packed
+    return layer_record(w, ms, stage_ms, hit, moe.moe_plan_describe(cfg)[0]), idx
+
+
+def skew_inputs(w, seed, dev, torch, target=0.90):
+    """The skewed layer's inputs with router row 0 = alpha * m, alpha bisected on
+    the library's own routing (zero bias) so that `target` of the tokens pick
+    expert 0."""
+    import mixture_experts_ffn_biased_amd as moe
+    from synthetic import make_inputs
+    inp = make_inputs(w, seed=seed, device=dev, expert0_scale=1.0)
+    cfg = moe.MoeConfig.from_workload(w)
+    m = inp["skew_dir"]
+    ws = moe.alloc_workspace(cfg, dev)
+
+    def share(alpha):
+        inp["W_router"][0] = (float(alpha) * m).to(inp["W_router"].dtype)
+        idx = moe.moe_route_debug(inp["u"], inp["W_router"], None, cfg=cfg, workspace=ws)[0]
+        return (idx == 0).any(dim=1).float().mean().item()
+    lo, hi = 0.0, 1.0
+    while share(hi) < target and hi < 1e3:
+        hi *= 2
+    for _ in range(30):
+        mid = 0.5 * (lo + hi)
+        lo, hi = (mid, hi) if share(mid) < target else (lo, mid)
+    got = share(hi)
+    return inp, hi, got
+
+
+def other_configs(args, torch, dev):
+    """Informational timings of the other layer shapes (packed weights)."""
+    import mixture_experts_ffn_biased_amd as moe
+    from synthetic import EP_SHARD, WORKLOADS, make_inputs
+    out = {}
+    w = WORKLOADS["mixtral_e8_top2"]
+    log(f"[bench] {w.name}")
+    inp = make_inputs(w, seed=args.seed, device=dev)
+    out[w.name], _ = time_shape(w, inp, args.steps, args.warmup, torch)
+    del inp
+    w = EP_SHARD
+    log(f"[bench] {w.name}")
+    inp = make_inputs(w, seed=args.seed, device=dev)
+    out[w.name], _ = time_shape(w, inp, args.steps, args.warmup, torch)
+    del inp
+    w = WORKLOADS["skewed_e128_top8"]
+    log(f"[bench] {w.name}: calibrating the skew on the library's routing")
+    inp, alpha, got = skew_inputs(w, args.seed, dev, torch)
+    rec_a, idx = time_shape(w, inp, args.steps, args.warmup, torch)
+    rec_a.update(bias="zero", expert0_scale=round(alpha, 4), expert0_share=round(got, 4),
+                 expert0_rows=int((idx == 0).sum().item()))
+    # the aux-loss-free balance loop on the device: 10 steps of +-0.15 from zero
+    cfg = moe.MoeConfig.from_workload(w)
+    ws = moe.alloc_workspace(cfg, dev)
+    b = torch.zeros(w.E, dtype=torch.float32, device=dev)
+    for _ in range(10):
+        idx = moe.moe_route_debug(inp["u"], inp["W_router"], b, cfg=cfg, workspace=ws)[0]
+        moe.moe_balance_update(idx, b, E=w.E, gamma=0.15)
+    rec_b, idx = time_shape(w, inp, args.steps, args.warmup, torch, bias=b)
+    rec_b.update(bias="10 on-device balance steps, gamma 0.15",
+                 expert0_rows=int((idx == 0).sum().item()))
+    out[w.name + "_a"] = rec_a
+    out[w.name + "_b"] = rec_b
+    del inp, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, inp, n_tokens, seed):
@@ -331,6 +427,9 @@ def main():
         result["plain_weights"] = {"ms_per_step": round(pms, 4),
                                    "tokens_per_s": round(w.T / (pms * 1e-3), 1),
                                    "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, pstage)}}
+
+    if not args.no_others:
+        result["other_configs"] = other_configs(args, torch, dev)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20

@@ -86,6 +86,13 @@ WORKLOADS = {
 }
 
 
+# One GPU's share of the DeepSeek-V3 layer under expert parallelism over 8
+# GPUs: 32 local experts that receive about 2048 token rows each (8192
+# local tokens x top-8 over 32 experts), plus the replicated shared expert on
+# the local tokens.  Measured as an extra shape, not a parity workload.
+EP_SHARD = Workload("ep_shard_e32", 8192, 7168, 32, 8, 2048, 2048, "sigmoid", 1, 1, 2.5, "bf16", "uniform")
+
+
 def _gen(seed: int, name: str, device) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(int(seed) * 1_000_003 + TENSOR_IDS[name] + 1)
