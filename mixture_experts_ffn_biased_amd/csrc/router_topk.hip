@@ -495,6 +495,12 @@ __global__ __launch_bounds__(256, 2) void router_logits_split(
 }
 
 // One wave per token: logits = sum of the splits in order, then selection.
+// One wave per token.  NSC = the split count rounded up to a multiple of 4:
+// every partial of the wave's experts is loaded before any is added (loads
+// past the last split re-read it and add +0, which changes nothing), so the
+// partial sums cost one memory round trip, not one per split.  The sum order
+// is fixed: four running sums over splits sp % 4, then (v0 + v1) + (v2 + v3).
+template <int NSC>
 __global__ __launch_bounds__(256) void router_select(const float *__restrict__ part, int nsplit,
                                                      int64_t T, SelArgs sel,
                                                      int32_t *__restrict__ topk_idx,
@@ -502,20 +508,28 @@ __global__ __launch_bounds__(256) void router_select(const float *__restrict__ p
   __shared__ float lg[4][kLogitStride];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = sel.E;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * 16 + wave; t < T && t < (blockIdx.x + 1) * 16LL;
-       t += 4) {
-    for (int e = lane; e < E; e += 64) {
-      // four independent partial sums (splits sp % 4), added in a fixed order
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      int sp = 0;
-      for (; sp + 4 <= nsplit; sp += 4)
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (t >= T) return;
+  constexpr int P = kMaxExperts / 64;
+  float x[P][NSC];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] += part[(static_cast<int64_t>(sp + i) * T + t) * E + e];
-      for (int i = 0; sp + i < nsplit; ++i) v[i] += part[(static_cast<int64_t>(sp + i) * T + t) * E + e];
-      lg[wave][e] = (v[0] + v[1]) + (v[2] + v[3]);
+  for (int p = 0; p < P; ++p) {
+    const int e = lane + 64 * p < E ? lane + 64 * p : E - 1;
+#pragma unroll
+    for (int sp = 0; sp < NSC; ++sp) {
+      const int spc = sp < nsplit ? sp : nsplit - 1;
+      x[p][sp] = part[(static_cast<int64_t>(spc) * T + t) * E + e];
     }
-    select_token(lg[wave], sel, topk_idx + t * sel.k, gates + t * sel.k);
   }
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int e = lane + 64 * p;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < NSC; ++sp) v[sp & 3] += sp < nsplit ? x[p][sp] : 0.f;
+    if (e < E) lg[wave][e] = (v[0] + v[1]) + (v[2] + v[3]);
+  }
+  select_token(lg[wave], sel, topk_idx + t * sel.k, gates + t * sel.k);
 }
 
 }  // namespace
@@ -551,8 +565,15 @@ hipError_t launch_router_topk(const Plan &p, const void *u, const void *Wr, cons
       hipLaunchKernelGGL(router_logits_split<4>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(router_select, dim3(static_cast<unsigned>((c.T + 15) / 16)), dim3(256), 0, s,
-                       p.router_part, S, c.T, sel, topk_idx, gates);
+    const dim3 sgrid(static_cast<unsigned>((c.T + 3) / 4));
+    if (S <= 4)
+      hipLaunchKernelGGL(router_select<4>, sgrid, dim3(256), 0, s, p.router_part, S, c.T, sel, topk_idx, gates);
+    else if (S <= 8)
+      hipLaunchKernelGGL(router_select<8>, sgrid, dim3(256), 0, s, p.router_part, S, c.T, sel, topk_idx, gates);
+    else if (S <= 12)
+      hipLaunchKernelGGL(router_select<12>, sgrid, dim3(256), 0, s, p.router_part, S, c.T, sel, topk_idx, gates);
+    else
+      hipLaunchKernelGGL(router_select<16>, sgrid, dim3(256), 0, s, p.router_part, S, c.T, sel, topk_idx, gates);
     return hipGetLastError();
   }
   if (c.dtype == MOE_BF16 && c.d % 128 == 0) {
