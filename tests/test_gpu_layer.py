@@ -99,6 +99,11 @@ SMALL = {
                                      1.0, "bf16", "uniform"),
     "e256_groups_bf16": Workload("e256_groups_bf16", 150, 128, 256, 8, 64, 64, "sigmoid", 8, 4, 2.5,
                                  "bf16", "uniform"),
+    # the largest top-k the library takes (32)
+    "max_k32_bf16": Workload("max_k32_bf16", 90, 128, 64, 32, 64, 0, "softmax", 1, 1, 1.0, "bf16", "uniform"),
+    # the largest group count (64 groups of 4, keep 8)
+    "groups64_sigmoid_bf16": Workload("groups64_sigmoid_bf16", 120, 128, 256, 16, 64, 64, "sigmoid", 64, 8,
+                                      2.5, "bf16", "uniform"),
 }
 
 
@@ -324,6 +329,17 @@ def test_dsv3_decode_full_size(dev):
     w = WORKLOADS["dsv3_decode"]
     inp = make_inputs(w, seed=0, device=dev)
     check_large(w, inp, n_sample=24)
+    del inp
+
+
+def test_streaming_schedule_overflow_falls_back_to_the_tiled_kernels(dev):
+    """720,000 tokens: more expert chunks than the streaming schedule holds, so
+    the layer runs on the tiled kernels (11,258 tiles); routing of every token
+    and sampled outputs against the oracle."""
+    w = Workload("huge_t", 720_000, 256, 8, 2, 128, 0, "softmax", 1, 1, 1.0, "bf16", "zero")
+    assert moe.moe_plan_describe(moe.MoeConfig.from_workload(w))[0] == "tiled"
+    inp = make_inputs(w, seed=4, device=dev)
+    check_large(w, inp, n_sample=16, must_include=np.array([0, w.T - 1]))
     del inp
 
 
