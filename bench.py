@@ -218,8 +218,8 @@ def skew_inputs(w, seed, dev, torch, target=0.90):
 
 
 def expert_bodies(w, inp, args, torch):
-    """The same layer with GEGLU experts and with biased GELU-MLP experts
-    (plain weight layout, moe_layer_forward_ex)."""
+    """The same layer with GEGLU experts and with biased GELU-MLP experts, on
+    weights packed for each body (moe_pack_weights_ex, not timed)."""
     import mixture_experts_ffn_biased_amd as moe
     from synthetic import make_ffn_biases
     cfg = moe.MoeConfig.from_workload(w)
@@ -228,28 +228,29 @@ def expert_bodies(w, inp, args, torch):
     y = torch.empty_like(inp["u"])
     idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
     gates = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    W1s, W3s, W2s = inp["shared"]
     out = {}
     for kind in ("geglu", "gelu_mlp"):
         gated = kind == "geglu"
+        packed = moe.moe_pack_weights_ex(kind, inp["W1"], inp["W3"] if gated else None, inp["W2"],
+                                         (W1s, W3s if gated else None, W2s), cfg=cfg)
         ws = torch.empty(max(moe.moe_workspace_bytes_ex(cfg, kind), 256), dtype=torch.uint8, device=dev)
-        W1s, W3s, W2s = inp["shared"]
-        shared = (W1s, W3s, W2s) if gated else (W1s, None, W2s, fb["b1s"], fb["b2s"])
+        b = (None,) * 4 if gated else (fb["b1"], fb["b2"], fb["b1s"], fb["b2s"])
 
         def step():
-            moe.moe_layer_forward_ex(inp["u"], inp["W_router"], inp["bias"], kind, inp["W1"],
-                                     inp["W3"] if gated else None, inp["W2"], None if gated else fb["b1"],
-                                     None if gated else fb["b2"], shared, cfg=cfg, y=y, topk_idx=idx,
-                                     gates=gates, workspace=ws)
-        ms, _, stage_ms, _ = timed_steps(step, max(3, args.steps // 2), 2, torch)
+            moe.moe_layer_forward_packed_ex(inp["u"], inp["W_router"], inp["bias"], kind, packed, *b, cfg=cfg, y=y,
+                                            topk_idx=idx, gates=gates, workspace=ws)
+        ms, _, stage_ms, _ = timed_steps(step, args.steps, args.warmup, torch)
         # FLOPs: router + (6 or 4) d F per routed slot and per token for the shared expert
         per = 6.0 if gated else 4.0
         flops = w.T * (2.0 * w.d * w.E + per * w.d * w.F * w.k + per * w.d * w.Fs)
         tf = flops / (ms * 1e-3) / 1e12
         out[kind] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
                      "layer_tflops": round(tf, 2), "layer_mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                     "gemm_path": moe.moe_plan_describe_ex(cfg, kind)[0], "weights": "plain",
+                     "gemm_path": moe.moe_plan_describe_ex(cfg, kind)[0], "weights": "packed",
                      "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, stage_ms)}}
-        del ws
+        del ws, packed
+        torch.cuda.empty_cache()
     return out
 
 
@@ -464,7 +465,7 @@ def main():
                                    "tokens_per_s": round(w.T / (pms * 1e-3), 1),
                                    "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, pstage)}}
 
-    if packed is not None and not args.no_plain:
+    if packed is not None:
         result["expert_bodies"] = expert_bodies(w, inp, args, torch)
 
     if not args.no_others:

@@ -176,10 +176,22 @@ moe_status moe_layer_forward_packed(const void *u, const void *W_router, const f
  *   0 when cfg or kind is invalid (for SwiGLU, moe_workspace_bytes(cfg)).
  * moe_plan_describe_ex: moe_plan_describe for the given kind.  The GELU MLP
  *   takes the streaming kernels only with F % 256 == 0 and F_shared % 256 == 0.
- * moe_layer_forward_ex: moe_layer_forward with these experts (plain layout;
- *   the packed layout serves SwiGLU only).  For bf16 the hidden activations
- *   after the activation (and the bias b1) and the per-slot expert outputs
- *   (with b2) are stored as bf16.  MOE_ERR_DTYPE for an unknown kind.
+ * moe_layer_forward_ex: moe_layer_forward with these experts (plain layout).
+ *   For bf16 the hidden activations after the activation (and the bias b1)
+ *   and the per-slot expert outputs (with b2) are stored as bf16.
+ *   MOE_ERR_DTYPE for an unknown kind.
+ *
+ * Packed weights for these bodies (the layout of moe_pack_weights; the GELU
+ * MLP's gate/up region holds W1 alone, in 256-row slabs like W2):
+ * moe_packed_weights_bytes_ex: size for cfg and kind, 0 when cfg cannot be
+ *   packed (d, F, F_shared multiples of 256, bf16) or kind is unknown.
+ * moe_pack_weights_ex: packs the weight pointers of *experts (its biases are
+ *   not packed and not read) into packed, enqueued on stream.
+ * moe_layer_forward_packed_ex: moe_layer_forward_ex with the packed buffer in
+ *   place of the weights: experts->kind and its bias pointers are read (the
+ *   kind must be the one packed), its weight pointers are not.  The result is
+ *   bitwise that of moe_layer_forward_ex.  MOE_ERR_SHAPE when cfg cannot be
+ *   packed or T is too large for the streaming schedule.
  */
 typedef enum { MOE_EXPERT_SWIGLU = 0, MOE_EXPERT_GEGLU = 1, MOE_EXPERT_GELU_MLP = 2 } moe_expert_kind;
 
@@ -203,6 +215,13 @@ moe_status moe_layer_forward_ex(const void *u, const void *W_router, const float
                                 const moe_experts *experts, const moe_cfg *cfg, void *y,
                                 int32_t *topk_idx, float *gates, void *workspace,
                                 size_t workspace_bytes, void *stream);
+size_t moe_packed_weights_bytes_ex(const moe_cfg *cfg, int32_t kind);
+moe_status moe_pack_weights_ex(const moe_cfg *cfg, const moe_experts *experts, void *packed,
+                               size_t packed_bytes, void *stream);
+moe_status moe_layer_forward_packed_ex(const void *u, const void *W_router, const float *bias,
+                                       const moe_experts *experts, const void *packed,
+                                       const moe_cfg *cfg, void *y, int32_t *topk_idx, float *gates,
+                                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Routing and permutation only (the first two stages of moe_layer_forward,

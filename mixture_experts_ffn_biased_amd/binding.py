@@ -136,6 +136,13 @@ def lib():
         L.moe_plan_describe_ex.restype = I32
         L.moe_layer_forward_ex.argtypes = [P, P, P, ctypes.POINTER(moe_experts), CP, P, P, P, P, SZ, P]
         L.moe_layer_forward_ex.restype = I32
+        L.moe_packed_weights_bytes_ex.argtypes = [CP, I32]
+        L.moe_packed_weights_bytes_ex.restype = SZ
+        L.moe_pack_weights_ex.argtypes = [CP, ctypes.POINTER(moe_experts), P, SZ, P]
+        L.moe_pack_weights_ex.restype = I32
+        L.moe_layer_forward_packed_ex.argtypes = [P, P, P, ctypes.POINTER(moe_experts), P, CP, P, P, P, P,
+                                                  SZ, P]
+        L.moe_layer_forward_packed_ex.restype = I32
         L.moe_status_str.argtypes = [I32]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_timing_enable.argtypes = [I32]
@@ -264,18 +271,10 @@ def moe_layer_forward(u, W_router, bias, W1, W3, W2, shared: Optional[Sequence] 
     return y, topk_idx, gates
 
 
-def moe_layer_forward_ex(u, W_router, bias, kind, W1, W3, W2, b1=None, b2=None, shared=None, *,
-                         cfg: MoeConfig, y=None, topk_idx=None, gates=None, workspace=None, stream=None):
-    """moe_layer_forward with experts of the given kind ("swiglu", "geglu", "gelu_mlp").
-
-    W3 is None for the GELU MLP; b1 [E][F] and b2 [E][d] (GELU MLP only) may be None.
-    shared: None or (W1s, W3s, W2s[, b1s, b2s])."""
-    kd = _kind(kind)
-    dev = u.device
+def _experts(cfg, kind, W1, W3, W2, b1, b2, shared, dev):
+    """Checks the expert tensors and builds the moe_experts struct."""
     dt = cfg.torch_dtype
-    T, d, E, k, F, Fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.F_shared
-    _need(u, (T, d), dt, "u", dev)
-    _need(W_router, (E, d), dt, "W_router", dev)
+    E, d, F, Fs = cfg.E, cfg.d, cfg.F, cfg.F_shared
     _need(W1, (E, F, d), dt, "W1", dev)
     if W3 is not None:
         _need(W3, (E, F, d), dt, "W3", dev)
@@ -284,9 +283,7 @@ def moe_layer_forward_ex(u, W_router, bias, kind, W1, W3, W2, b1=None, b2=None, 
         _need(b1, (E, F), dt, "b1", dev)
     if b2 is not None:
         _need(b2, (E, d), dt, "b2", dev)
-    if bias is not None:
-        _need(bias, (E,), torch.float32, "bias", dev)
-    ex = moe_experts(kd, *(None if t is None else t.data_ptr() for t in (W1, W3, W2, b1, b2)))
+    ex = moe_experts(_kind(kind), *(None if t is None else t.data_ptr() for t in (W1, W3, W2, b1, b2)))
     if shared is not None:
         sh = list(shared) + [None] * (5 - len(shared))
         W1s, W3s, W2s, b1s, b2s = sh
@@ -300,6 +297,25 @@ def moe_layer_forward_ex(u, W_router, bias, kind, W1, W3, W2, b1=None, b2=None, 
             _need(b2s, (d,), dt, "b2s", dev)
         for name, t in zip(("W1s", "W3s", "W2s", "b1s", "b2s"), sh):
             setattr(ex, name, None if t is None else t.data_ptr())
+    return ex
+
+
+def _bias_struct(cfg, kind, b1, b2, b1s, b2s, dev):
+    """moe_experts with only the kind and the biases (for the packed forward)."""
+    dt = cfg.torch_dtype
+    for t, shape, name in ((b1, (cfg.E, cfg.F), "b1"), (b2, (cfg.E, cfg.d), "b2"),
+                           (b1s, (cfg.F_shared,), "b1s"), (b2s, (cfg.d,), "b2s")):
+        if t is not None:
+            _need(t, shape, dt, name, dev)
+    ex = moe_experts(_kind(kind))
+    for name, t in (("b1", b1), ("b2", b2), ("b1s", b1s), ("b2s", b2s)):
+        setattr(ex, name, None if t is None else t.data_ptr())
+    return ex
+
+
+def _layer_outputs(cfg, dev, y, topk_idx, gates):
+    dt = cfg.torch_dtype
+    T, d, k = cfg.T, cfg.d, cfg.k
     if y is None:
         y = torch.empty((T, d), dtype=dt, device=dev)
     if topk_idx is None:
@@ -309,17 +325,84 @@ def moe_layer_forward_ex(u, W_router, bias, kind, W1, W3, W2, b1=None, b2=None, 
     _need(y, (T, d), dt, "y", dev)
     _need(topk_idx, (T, k), torch.int32, "topk_idx", dev)
     _need(gates, (T, k), torch.float32, "gates", dev)
+    return y, topk_idx, gates
+
+
+def _workspace_ex(cfg, kind, dev, workspace):
     if workspace is None:
-        n = moe_workspace_bytes_ex(cfg, kd)
-        if n == 0 and T > 0:
+        n = moe_workspace_bytes_ex(cfg, kind)
+        if n == 0 and cfg.T > 0:
             raise MoeError(moe_check_cfg(cfg) or -4, "moe_workspace_bytes_ex")
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def moe_layer_forward_ex(u, W_router, bias, kind, W1, W3, W2, b1=None, b2=None, shared=None, *,
+                         cfg: MoeConfig, y=None, topk_idx=None, gates=None, workspace=None, stream=None):
+    """moe_layer_forward with experts of the given kind ("swiglu", "geglu", "gelu_mlp").
+
+    W3 is None for the GELU MLP; b1 [E][F] and b2 [E][d] (GELU MLP only) may be None.
+    shared: None or (W1s, W3s, W2s[, b1s, b2s])."""
+    dev = u.device
+    _need(u, (cfg.T, cfg.d), cfg.torch_dtype, "u", dev)
+    _need(W_router, (cfg.E, cfg.d), cfg.torch_dtype, "W_router", dev)
+    if bias is not None:
+        _need(bias, (cfg.E,), torch.float32, "bias", dev)
+    ex = _experts(cfg, kind, W1, W3, W2, b1, b2, shared, dev)
+    y, topk_idx, gates = _layer_outputs(cfg, dev, y, topk_idx, gates)
+    workspace = _workspace_ex(cfg, kind, dev, workspace)
     c = cfg.to_c()
     st = lib().moe_layer_forward_ex(_ptr(u), _ptr(W_router), _ptr(bias), ctypes.byref(ex), ctypes.byref(c),
                                     _ptr(y), _ptr(topk_idx), _ptr(gates), _ptr(workspace), workspace.numel(),
                                     _stream(dev, stream))
     if st != 0:
         raise MoeError(st, "moe_layer_forward_ex")
+    return y, topk_idx, gates
+
+
+def moe_packed_weights_bytes_ex(cfg: MoeConfig, kind) -> int:
+    c = cfg.to_c()
+    return int(lib().moe_packed_weights_bytes_ex(ctypes.byref(c), _kind(kind)))
+
+
+def moe_pack_weights_ex(kind, W1, W3, W2, shared=None, *, cfg: MoeConfig, packed=None, stream=None):
+    """One-time re-layout of the weights of experts of the given kind; returns
+    the packed uint8 buffer (biases are not packed).  shared: None or
+    (W1s, W3s, W2s); W3 / W3s None for the GELU MLP."""
+    dev = W1.device
+    ex = _experts(cfg, kind, W1, W3, W2, None, None, None if shared is None else tuple(shared)[:3], dev)
+    n = moe_packed_weights_bytes_ex(cfg, kind)
+    if n == 0:
+        raise MoeError(-2, "moe_packed_weights_bytes_ex")
+    if packed is None:
+        packed = torch.empty(n, dtype=torch.uint8, device=dev)
+    c = cfg.to_c()
+    st = lib().moe_pack_weights_ex(ctypes.byref(c), ctypes.byref(ex), _ptr(packed), packed.numel(),
+                                   _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_pack_weights_ex")
+    return packed
+
+
+def moe_layer_forward_packed_ex(u, W_router, bias, kind, packed, b1=None, b2=None, b1s=None, b2s=None, *,
+                                cfg: MoeConfig, y=None, topk_idx=None, gates=None, workspace=None,
+                                stream=None):
+    """moe_layer_forward_ex on weights packed by moe_pack_weights_ex for the same kind."""
+    dev = u.device
+    _need(u, (cfg.T, cfg.d), cfg.torch_dtype, "u", dev)
+    _need(W_router, (cfg.E, cfg.d), cfg.torch_dtype, "W_router", dev)
+    if bias is not None:
+        _need(bias, (cfg.E,), torch.float32, "bias", dev)
+    _need(packed, (moe_packed_weights_bytes_ex(cfg, kind),), torch.uint8, "packed", dev)
+    ex = _bias_struct(cfg, kind, b1, b2, b1s, b2s, dev)
+    y, topk_idx, gates = _layer_outputs(cfg, dev, y, topk_idx, gates)
+    workspace = _workspace_ex(cfg, kind, dev, workspace)
+    c = cfg.to_c()
+    st = lib().moe_layer_forward_packed_ex(_ptr(u), _ptr(W_router), _ptr(bias), ctypes.byref(ex), _ptr(packed),
+                                           ctypes.byref(c), _ptr(y), _ptr(topk_idx), _ptr(gates),
+                                           _ptr(workspace), workspace.numel(), _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_layer_forward_packed_ex")
     return y, topk_idx, gates
 
 

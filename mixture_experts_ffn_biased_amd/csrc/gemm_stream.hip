@@ -600,36 +600,42 @@ int stream_max_chunks() { return kMaxChunks; }
 int stream_nslab_gate_up(int F, int kind) { return kind == MOE_EXPERT_GELU_MLP ? F / SBN : F / (SBN / 2); }
 int stream_nslab_down(int d) { return d / SBN; }
 
-size_t packed_weights_bytes(const moe_cfg &c) {
-  return 2ull * (2ull * c.E * c.F * c.d + static_cast<size_t>(c.E) * c.d * c.F + 2ull * c.F_shared * c.d +
+// Packed regions: routed gate/up, routed down, shared gate/up, shared down.
+// The gated bodies pack W1 and W3 together (2 F rows a matrix), the GELU MLP
+// W1 alone (F rows, 256-row slabs like down).
+size_t packed_weights_bytes(const moe_cfg &c, int kind) {
+  const size_t g = kind == MOE_EXPERT_GELU_MLP ? 1 : 2;
+  return 2ull * (g * c.E * c.F * c.d + static_cast<size_t>(c.E) * c.d * c.F + g * c.F_shared * c.d +
                  static_cast<size_t>(c.d) * c.F_shared);
 }
 
-PackedView packed_view(const moe_cfg &c, const void *base) {
+PackedView packed_view(const moe_cfg &c, int kind, const void *base) {
+  const size_t g = kind == MOE_EXPERT_GELU_MLP ? 1 : 2;
   const char *b = static_cast<const char *>(base);
   PackedView v;
   v.gu = b;
-  v.dn = b + 4ull * c.E * c.F * c.d;
+  v.dn = b + 2ull * g * c.E * c.F * c.d;
   v.gu_s = static_cast<const char *>(v.dn) + 2ull * c.E * c.d * c.F;
-  v.dn_s = static_cast<const char *>(v.gu_s) + 4ull * c.F_shared * c.d;
+  v.dn_s = static_cast<const char *>(v.gu_s) + 2ull * g * c.F_shared * c.d;
   return v;
 }
 
-hipError_t launch_pack_weights(const moe_cfg &c, const void *W1, const void *W3, const void *W2,
+hipError_t launch_pack_weights(const moe_cfg &c, int kind, const void *W1, const void *W3, const void *W2,
                                const void *W1s, const void *W3s, const void *W2s, void *packed,
                                hipStream_t s) {
-  const PackedView v = packed_view(c, packed);
-  auto run = [&](const void *a, const void *b, int dual, int64_t n, int rows, int K, const void *out) {
-    const int64_t chunks = n * static_cast<int64_t>(rows) * K * (dual ? 2 : 1) / 8;
+  const PackedView v = packed_view(c, kind, packed);
+  const int dual = kind == MOE_EXPERT_GELU_MLP ? 0 : 1;
+  auto run = [&](const void *a, const void *b, int du, int64_t n, int rows, int K, const void *out) {
+    const int64_t chunks = n * static_cast<int64_t>(rows) * K * (du ? 2 : 1) / 8;
     const unsigned blocks = static_cast<unsigned>(chunks / 256 < 65536 ? (chunks + 255) / 256 : 65536);
     hipLaunchKernelGGL(pack_weights, dim3(blocks), dim3(256), 0, s, static_cast<const uint16_t *>(a),
-                       static_cast<const uint16_t *>(b), dual, n, rows, K,
+                       static_cast<const uint16_t *>(b), du, n, rows, K,
                        static_cast<uint16_t *>(const_cast<void *>(out)));
     return hipGetLastError();
   };
-  hipError_t e = run(W1, W3, 1, c.E, c.F, c.d, v.gu);
+  hipError_t e = run(W1, dual ? W3 : nullptr, dual, c.E, c.F, c.d, v.gu);
   if (e == hipSuccess) e = run(W2, nullptr, 0, c.E, c.d, c.F, v.dn);
-  if (e == hipSuccess && c.F_shared > 0) e = run(W1s, W3s, 1, 1, c.F_shared, c.d, v.gu_s);
+  if (e == hipSuccess && c.F_shared > 0) e = run(W1s, dual ? W3s : nullptr, dual, 1, c.F_shared, c.d, v.gu_s);
   if (e == hipSuccess && c.F_shared > 0) e = run(W2s, nullptr, 0, 1, c.d, c.F_shared, v.dn_s);
   return e;
 }
@@ -645,15 +651,17 @@ hipError_t launch_stream_schedule(const Plan &p, hipStream_t s) {
 
 typedef void (*stream_kernel_t)(StreamArgs);
 
-// The kernel of one variant for an epilogue; the packed layout only with the
-// SwiGLU epilogues (null otherwise).
+// The kernel of one variant for an epilogue and weight layout.
 template <int VAR>
 static stream_kernel_t pick_kernel(int epi, bool packed) {
 #define MOE_STREAM_K(E, P) (VAR == 0 ? gemm_stream_prefill<E, P> : gemm_stream_decode<E, P>)
   if (packed) {
     switch (epi) {
       case EPI_SILU_GLU: return MOE_STREAM_K(EPI_SILU_GLU, true);
+      case EPI_GELU_GLU: return MOE_STREAM_K(EPI_GELU_GLU, true);
       case EPI_PLAIN: return MOE_STREAM_K(EPI_PLAIN, true);
+      case EPI_BIAS: return MOE_STREAM_K(EPI_BIAS, true);
+      case EPI_BIAS_GELU: return MOE_STREAM_K(EPI_BIAS_GELU, true);
       default: return nullptr;
     }
   }

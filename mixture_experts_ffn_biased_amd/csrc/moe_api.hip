@@ -286,48 +286,102 @@ moe_status moe_layer_forward(const void *u, const void *W_router, const float *b
                    static_cast<hipStream_t>(stream));
 }
 
+}  // extern "C"
+
+// Checks an expert description against cfg and fills *x.  weights: its weight
+// pointers are read (plain layout, or the source of a packing); otherwise
+// only the kind and the biases are.
+static moe_status check_experts(const moe_experts *experts, const moe_cfg *cfg, bool weights, Experts *x) {
+  if (!experts) return MOE_ERR_NULL;
+  const moe_experts &e = *experts;
+  if (!valid_kind(e.kind)) return MOE_ERR_DTYPE;
+  const bool gated = e.kind != MOE_EXPERT_GELU_MLP;
+  const bool has_shared = cfg->F_shared > 0;
+  if (weights && has_shared != (e.W1s || e.W3s || e.W2s)) return MOE_ERR_CFG;
+  if (gated && (e.b1 || e.b2 || e.b1s || e.b2s)) return MOE_ERR_CFG;
+  if (!has_shared && (e.b1s || e.b2s)) return MOE_ERR_CFG;
+  *x = Experts{};
+  x->kind = e.kind;
+  x->b1 = e.b1;
+  x->b2 = e.b2;
+  x->b1s = e.b1s;
+  x->b2s = e.b2s;
+  if (weights) {
+    if (!e.W1 || !e.W2 || (gated && !e.W3)) return MOE_ERR_NULL;
+    if (has_shared && (!e.W1s || !e.W2s || (gated && !e.W3s))) return MOE_ERR_NULL;
+    x->W1 = e.W1;
+    x->W3 = gated ? e.W3 : nullptr;
+    x->W2 = e.W2;
+    x->W1s = e.W1s;
+    x->W3s = gated ? e.W3s : nullptr;
+    x->W2s = e.W2s;
+  }
+  const void *ptrs[] = {x->W1, x->W2, x->W3, x->b1, x->b2, x->W1s, x->W2s, x->W3s, x->b1s, x->b2s};
+  for (const void *q : ptrs)
+    if (q && !aligned16(q)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+extern "C" {
+
 moe_status moe_layer_forward_ex(const void *u, const void *W_router, const float *bias,
                                 const moe_experts *experts, const moe_cfg *cfg, void *y, int32_t *topk_idx,
                                 float *gates, void *workspace, size_t workspace_bytes, void *stream) {
   moe_status st = validate(cfg);
   if (st != MOE_OK) return st;
-  if (!experts) return MOE_ERR_NULL;
-  const moe_experts &e = *experts;
-  if (!valid_kind(e.kind)) return MOE_ERR_DTYPE;
-  const bool gated = e.kind != MOE_EXPERT_GELU_MLP;
-  const bool has_shared = e.W1s || e.W3s || e.W2s;
-  if ((cfg->F_shared > 0) != has_shared) return MOE_ERR_CFG;
-  if (gated && (e.b1 || e.b2 || e.b1s || e.b2s)) return MOE_ERR_CFG;
-  if (!has_shared && (e.b1s || e.b2s)) return MOE_ERR_CFG;
-  if (cfg->T == 0) return MOE_OK;
-  if (!e.W1 || !e.W2 || (gated && !e.W3)) return MOE_ERR_NULL;
-  if (has_shared && (!e.W1s || !e.W2s || (gated && !e.W3s))) return MOE_ERR_NULL;
-  const void *ptrs[] = {e.W1, e.W2, e.W3, e.b1, e.b2, e.W1s, e.W2s, e.W3s, e.b1s, e.b2s};
-  for (const void *q : ptrs)
-    if (q && !aligned16(q)) return MOE_ERR_ALIGN;
+  Experts x;
+  st = check_experts(experts, cfg, cfg->T > 0, &x);
+  if (st != MOE_OK || cfg->T == 0) return st;
   Plan p;
-  st = check_forward(u, W_router, cfg, e.kind, y, topk_idx, gates, workspace, workspace_bytes, &p);
+  st = check_forward(u, W_router, cfg, x.kind, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
-  Experts x{};
-  x.kind = e.kind;
-  x.W1 = e.W1;
-  x.W3 = gated ? e.W3 : nullptr;
-  x.W2 = e.W2;
-  x.b1 = e.b1;
-  x.b2 = e.b2;
-  if (has_shared) {
-    x.W1s = e.W1s;
-    x.W3s = gated ? e.W3s : nullptr;
-    x.W2s = e.W2s;
-    x.b1s = e.b1s;
-    x.b2s = e.b2s;
-  }
   return run_layer(p, u, W_router, bias, x, nullptr, y, topk_idx, gates, static_cast<hipStream_t>(stream));
 }
 
-size_t moe_packed_weights_bytes(const moe_cfg *cfg) {
-  if (validate(cfg) != MOE_OK || !packable(*cfg)) return 0;
-  return packed_weights_bytes(*cfg);
+moe_status moe_pack_weights_ex(const moe_cfg *cfg, const moe_experts *experts, void *packed, size_t packed_bytes,
+                               void *stream) {
+  moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  Experts x;
+  st = check_experts(experts, cfg, true, &x);
+  if (st != MOE_OK) return st;
+  if (!packable(*cfg)) return MOE_ERR_SHAPE;
+  if (!packed) return MOE_ERR_NULL;
+  if (!aligned16(packed)) return MOE_ERR_ALIGN;
+  if (packed_bytes < packed_weights_bytes(*cfg, x.kind)) return MOE_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  if (launch_pack_weights(*cfg, x.kind, x.W1, x.W3, x.W2, x.W1s, x.W3s, x.W2s, packed,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward_packed_ex(const void *u, const void *W_router, const float *bias,
+                                       const moe_experts *experts, const void *packed, const moe_cfg *cfg, void *y,
+                                       int32_t *topk_idx, float *gates, void *workspace, size_t workspace_bytes,
+                                       void *stream) {
+  moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  Experts x;
+  st = check_experts(experts, cfg, false, &x);
+  if (st != MOE_OK) return st;
+  if (!packable(*cfg)) return MOE_ERR_SHAPE;
+  if (cfg->T == 0) return MOE_OK;
+  if (!packed) return MOE_ERR_NULL;
+  if (!aligned16(packed)) return MOE_ERR_ALIGN;
+  Plan p;
+  st = check_forward(u, W_router, cfg, x.kind, y, topk_idx, gates, workspace, workspace_bytes, &p);
+  if (st != MOE_OK) return st;
+  if (p.path == PATH_TILED) return MOE_ERR_SHAPE;  // too many tiles for the streaming schedule
+  const PackedView pk = packed_view(*cfg, x.kind, packed);
+  return run_layer(p, u, W_router, bias, x, &pk, y, topk_idx, gates, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_packed_weights_bytes(const moe_cfg *cfg) { return moe_packed_weights_bytes_ex(cfg, MOE_EXPERT_SWIGLU); }
+
+size_t moe_packed_weights_bytes_ex(const moe_cfg *cfg, int32_t kind) {
+  if (validate(cfg) != MOE_OK || !valid_kind(kind) || !packable(*cfg)) return 0;
+  return packed_weights_bytes(*cfg, kind);
 }
 
 moe_status moe_pack_weights(const moe_cfg *cfg, const void *W1, const void *W3, const void *W2,
@@ -338,13 +392,14 @@ moe_status moe_pack_weights(const moe_cfg *cfg, const void *W1, const void *W3, 
   if ((cfg->F_shared > 0) != (shared != nullptr)) return MOE_ERR_CFG;
   if (!W1 || !W3 || !W2 || !packed) return MOE_ERR_NULL;
   if (shared && (!shared->W1 || !shared->W3 || !shared->W2)) return MOE_ERR_NULL;
-  if (packed_bytes < packed_weights_bytes(*cfg)) return MOE_ERR_WORKSPACE;
+  if (packed_bytes < packed_weights_bytes(*cfg, MOE_EXPERT_SWIGLU)) return MOE_ERR_WORKSPACE;
   const void *ptrs[] = {W1, W3, W2, packed, shared ? shared->W1 : W1, shared ? shared->W3 : W1,
                         shared ? shared->W2 : W1};
   for (const void *q : ptrs)
     if (!aligned16(q)) return MOE_ERR_ALIGN;
   (void)hipGetLastError();
-  if (launch_pack_weights(*cfg, W1, W3, W2, shared ? shared->W1 : nullptr, shared ? shared->W3 : nullptr,
+  if (launch_pack_weights(*cfg, MOE_EXPERT_SWIGLU, W1, W3, W2, shared ? shared->W1 : nullptr,
+                          shared ? shared->W3 : nullptr,
                           shared ? shared->W2 : nullptr, packed, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return MOE_ERR_HIP;
@@ -365,7 +420,7 @@ moe_status moe_layer_forward_packed(const void *u, const void *W_router, const f
   st = check_forward(u, W_router, cfg, MOE_EXPERT_SWIGLU, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
   if (p.path == PATH_TILED) return MOE_ERR_SHAPE;  // too many tiles for the streaming schedule
-  const PackedView pk = packed_view(*cfg, packed);
+  const PackedView pk = packed_view(*cfg, MOE_EXPERT_SWIGLU, packed);
   // The shared expert is present iff F_shared > 0 (the kernels read pk).
   return run_layer(p, u, W_router, bias, swiglu_experts(nullptr, nullptr, nullptr, nullptr), &pk, y, topk_idx,
                    gates, static_cast<hipStream_t>(stream));
@@ -457,7 +512,7 @@ moe_status moe_block_forward_packed(const void *h, const void *norm_weight, floa
   (void)hipGetLastError();
   if (launch_rmsnorm(h, norm_weight, norm_eps, cfg->T, cfg->d, cfg->dtype, un, s) != hipSuccess)
     return MOE_ERR_HIP;
-  const PackedView pk = packed_view(*cfg, packed);
+  const PackedView pk = packed_view(*cfg, MOE_EXPERT_SWIGLU, packed);
   return run_layer(p, un, W_router, bias, swiglu_experts(nullptr, nullptr, nullptr, nullptr), &pk, y, topk_idx,
                    gates, s, h);
 }

@@ -133,14 +133,14 @@ int stream_max_chunks();
 int stream_tile_balanced(int path);
 int stream_nslab_gate_up(int F, int kind);
 int stream_nslab_down(int d);
-size_t packed_weights_bytes(const moe_cfg &c);
-PackedView packed_view(const moe_cfg &c, const void *base);
-hipError_t launch_pack_weights(const moe_cfg &c, const void *W1, const void *W3, const void *W2,
+size_t packed_weights_bytes(const moe_cfg &c, int kind);
+PackedView packed_view(const moe_cfg &c, int kind, const void *base);
+hipError_t launch_pack_weights(const moe_cfg &c, int kind, const void *W1, const void *W3, const void *W2,
                                const void *W1s, const void *W3s, const void *W2s, void *packed,
                                hipStream_t s);
 hipError_t launch_stream_schedule(const Plan &p, hipStream_t s);
 // pk == nullptr: the plain weights of x; else the packed buffer's regions
-// (SwiGLU only) and x's pointers are not read.
+// (x's weight pointers are not read; its biases are).
 hipError_t launch_stream_gate_up(const Plan &p, const void *u, const Experts &x, const PackedView *pk,
                                  hipStream_t s);
 hipError_t launch_stream_down(const Plan &p, const Experts &x, const PackedView *pk, hipStream_t s);

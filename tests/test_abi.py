@@ -237,3 +237,42 @@ def test_expert_body_arguments_are_checked_before_any_launch():
     assert moe.moe_plan_describe_ex(cfg(T=4096, d=256, E=8, k=2, F=512, n_groups=1, topk_groups=1),
                                     "gelu_mlp")[0] == "stream"
     assert moe.moe_plan_describe_ex(big, "geglu") == moe.moe_plan_describe(big)
+
+
+def test_packed_expert_body_sizes_and_argument_checks():
+    L = moe.lib()
+    f = ctypes.c_void_p
+    c = cfg(T=512, d=256, E=8, k=2, F=512, F_shared=256, n_groups=1, topk_groups=1)
+    E, d, F, Fs = c.E, c.d, c.F, c.F_shared
+    gated = 2 * (2 * E * F * d + E * d * F + 2 * Fs * d + d * Fs)
+    assert moe.moe_packed_weights_bytes_ex(c, "swiglu") == moe.moe_packed_weights_bytes(c) == gated
+    assert moe.moe_packed_weights_bytes_ex(c, "geglu") == gated
+    assert moe.moe_packed_weights_bytes_ex(c, "gelu_mlp") == 2 * (E * F * d + E * d * F + Fs * d + d * Fs)
+    assert moe.moe_packed_weights_bytes_ex(c, 9) == 0
+    assert moe.moe_packed_weights_bytes_ex(cfg(d=256, F=384), "gelu_mlp") == 0
+    p = {n: f(0x1000000 * (i + 1)) for i, n in enumerate(
+        ["W1", "W3", "W2", "b1", "b2", "W1s", "W3s", "W2s", "b1s", "b2s", "pk", "u", "Wr", "y", "idx", "g", "ws"])}
+    x = c.to_c()
+
+    def pack(kind=binding.MOE_EXPERT_GELU_MLP, nbytes=1 << 30, **over):
+        q = dict(p)
+        q.update(over)
+        ex = binding.moe_experts(kind, q["W1"], None, q["W2"], None, None, q["W1s"], None, q["W2s"])
+        return L.moe_pack_weights_ex(ctypes.byref(x), ctypes.byref(ex), q["pk"], nbytes, None)
+    assert pack(kind=4) == -4
+    assert pack(W2s=None) == -1
+    assert pack(kind=binding.MOE_EXPERT_GEGLU) == -1   # W3 missing for a gated body
+    assert pack(pk=None) == -1 and pack(pk=f(0xB000008)) == -7
+    assert pack(nbytes=16) == -5
+
+    def fwd(kind=binding.MOE_EXPERT_GELU_MLP, b1=None, b1s=None, ws_bytes=1 << 30):
+        ex = binding.moe_experts(kind, None, None, None, b1, None, None, None, None, b1s, None)
+        return L.moe_layer_forward_packed_ex(p["u"], p["Wr"], None, ctypes.byref(ex), p["pk"], ctypes.byref(x),
+                                             p["y"], p["idx"], p["g"], p["ws"], ws_bytes, None)
+    assert fwd(kind=binding.MOE_EXPERT_GEGLU, b1=p["b1"]) == -3  # biases with a gated body
+    assert fwd(b1=f(0x4000004)) == -7
+    assert fwd(ws_bytes=16) == -5
+    x0 = cfg(T=0, d=256, E=8, k=2, F=512, F_shared=256, n_groups=1, topk_groups=1).to_c()
+    ex = binding.moe_experts(binding.MOE_EXPERT_GELU_MLP)
+    assert L.moe_layer_forward_packed_ex(None, None, None, ctypes.byref(ex), None, ctypes.byref(x0), None, None,
+                                         None, None, 0, None) == 0

@@ -197,3 +197,27 @@ def test_gelu_mlp_dsv3_decode_shape_sampled(dev):
     err = rel_l2(widen_gpu(y)[tokens], yr)
     log(f"[experts] dsv3_decode gelu_mlp sampled rel_l2_max={err.max():.3e}")
     assert err.max() <= Y_TOL["bf16"], f"max rel-L2 {err.max():.3e}"
+
+
+@pytest.mark.parametrize("kind", ["geglu", "gelu_mlp"])
+@pytest.mark.parametrize("name", ["stream_bf16", "decode_bf16"])
+def test_packed_expert_bodies_are_bitwise_the_plain_layout(dev, name, kind):
+    """moe_pack_weights_ex + moe_layer_forward_packed_ex give exactly the
+    plain-layout result (the plain one is checked against the oracle above)."""
+    w = CASES[name]
+    cfg = moe.MoeConfig.from_workload(w)
+    inp = to_dev(make_inputs(w, seed=16, device="cpu"), dev)
+    fb = make_ffn_biases(w, seed=16, device="cpu")
+    fb = to_dev(fb, dev) if kind == "gelu_mlp" else no_biases(fb)
+    ref = run_ex(w, inp, kind, fb)
+    gated = kind != "gelu_mlp"
+    W1s, W3s, W2s = inp["shared"]
+    packed = moe.moe_pack_weights_ex(kind, inp["W1"], inp["W3"] if gated else None, inp["W2"],
+                                     (W1s, W3s if gated else None, W2s), cfg=cfg)
+    assert packed.numel() == moe.moe_packed_weights_bytes_ex(cfg, kind)
+    got = moe.moe_layer_forward_packed_ex(inp["u"], inp["W_router"], inp["bias"], kind, packed, fb["b1"], fb["b2"],
+                                          fb["b1s"], fb["b2s"], cfg=cfg)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b), (name, kind)
+    log(f"[experts] packed {name} {kind} bitwise equal")
