@@ -57,6 +57,8 @@ def parse():
                     help="skip the reference timing of the plain weight layout")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the informational timings of the other layer shapes")
+    ap.add_argument("--no-bodies", action="store_true",
+                    help="skip the informational timings of the GEGLU and GELU-MLP expert bodies")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB three times (a plain "
                          "copy kernel of known size, to scale hardware byte counters)")
@@ -465,7 +467,7 @@ def main():
                                    "tokens_per_s": round(w.T / (pms * 1e-3), 1),
                                    "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, pstage)}}
 
-    if packed is not None:
+    if packed is not None and not args.no_bodies:
         result["expert_bodies"] = expert_bodies(w, inp, args, torch)
 
     if not args.no_others:
