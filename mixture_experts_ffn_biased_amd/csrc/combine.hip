@@ -1,5 +1,6 @@
-// Stage 5: gate-weighted combine, y[t] = Z[t] + sum_j gates[t][j] * O[inv[t*k+j]].
-// Z and O are in the layer dtype; the sum is accumulated in fp32.
+// Stage 5: gate-weighted combine, y[t] = Z[t] + sum_j gates[t][j] * O[inv[t*k+j]]
+// (+ R[t], the block input, in the pre-norm block form).  Z, O and R are in
+// the layer dtype; the sum is accumulated in fp32, R added last.
 //
 // "Sparse MoE FFN" (DeepSeek-V3), eq. 12 and "Packed forward": the routed
 // outputs are scaled by their gates and summed, the shared output is added

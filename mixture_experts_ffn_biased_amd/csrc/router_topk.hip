@@ -6,10 +6,13 @@
 // u_t^T e_i).  bf16 inputs use the bf16 MFMA (products of bf16 values are
 // exact in fp32); fp32 inputs use fp32 FMA.
 //
-// bf16 layers with d a multiple of 128 run router_topk_stream: 64 tokens per
-// workgroup, tiles of the tokens and of all router rows staged through a
-// 4-slot LDS ring by direct global-to-LDS loads (three stages in flight).
-// Other layers run router_topk_bf16 / router_topk_f32 (register staging).
+// bf16 layers with d a multiple of 128 split the GEMM over K when few 64-token
+// tiles exist or K is long (router_logits_split writes fp32 partial logits,
+// router_select adds them in a fixed order and selects), else run
+// router_topk_stream: 64 tokens per workgroup, tiles of the tokens and of all
+// router rows staged through a 4-slot LDS ring by direct global-to-LDS loads
+// (three stages in flight).  Other layers run router_topk_bf16 /
+// router_topk_f32 (register staging).
 //
 // Selection ("The router in code"; "Sparse MoE FFN", "How it works",
 // Routing): s = l (softmax mode) or sigmoid(l); sb = s + bias; with groups,
