@@ -28,7 +28,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+
+// Round to nearest even in one gfx950 v_cvt_pk_bf16_f32 (two values per
+// instruction for the packed form).
+__device__ __forceinline__ uint16_t f32_to_bf16_hw(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+  const f32x2_hw v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw));
+}
+
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+// SiLU for the bf16 epilogues: x * rcp(1 + 2^(-x log2 e)) on the hardware
+// exp2 and reciprocal (about 1 ulp each, well inside the bf16 rounding that
+// follows); x -> -inf gives -0, x -> +inf gives x, NaN stays NaN.
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
 
 // GELU(x) = x Phi(x), Phi the standard normal CDF, through erf (exact form).
 __device__ __forceinline__ float gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }

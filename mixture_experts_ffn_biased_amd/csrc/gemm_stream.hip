@@ -308,7 +308,7 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
         const int row = mi * 32 + 8 * (r >> 2) + row_lane + (r & 3);
         const int col = wn * 32 + (lane & 31);
         const float a1 = acc[mi][0][r];
-        Ht[row * 128 + col] = f32_to_bf16((EPI == EPI_GELU_GLU ? gelu(a1) : silu(a1)) * acc[mi][1][r]);
+        Ht[row * 128 + col] = f32_to_bf16_hw((EPI == EPI_GELU_GLU ? gelu(a1) : silu_fast(a1)) * acc[mi][1][r]);
       }
     }
     __syncthreads();
@@ -348,7 +348,7 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
           float v = acc[mi][ni][r];
           if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) v += bv[ni];
           if (EPI == EPI_BIAS_GELU) v = gelu(v);
-          Ot[row * 256 + col] = f32_to_bf16(v);
+          Ot[row * 256 + col] = f32_to_bf16_hw(v);
         }
     }
     __syncthreads();

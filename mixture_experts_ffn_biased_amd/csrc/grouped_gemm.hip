@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16(GemmArgs g) {
         if (row >= tl.nrows || col >= N) continue;
         float v = acc[mi][ni][0][r];
         if (DUAL) {
-          v = (g.epi == EPI_GELU_GLU ? gelu(v) : silu(v)) * acc[mi][ni][NM - 1][r];
+          v = (g.epi == EPI_GELU_GLU ? gelu(v) : silu_fast(v)) * acc[mi][ni][NM - 1][r];
         } else {
           if (bias) v += bf16_to_f32(bias[col]);
           if (g.epi == EPI_BIAS_GELU) v = gelu(v);
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16(GemmArgs g) {
         if (f32_out)
           static_cast<float *>(C)[o] = v;
         else
-          static_cast<uint16_t *>(C)[o] = f32_to_bf16(v);
+          static_cast<uint16_t *>(C)[o] = f32_to_bf16_hw(v);
       }
 }
 
