@@ -41,6 +41,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
+// 4 x 4 transpose within each quad of lanes, to bf16.  Lane j = lane & 3
+// holds f[b] = rows b = 0..3 of its own column (the four lanes of a quad hold
+// four consecutive columns); it returns row (j & 1) * 2 + (j >> 1) of those
+// four columns, packed as 4 bf16 (low column first), so that a quad writes
+// four whole 8-byte row pieces instead of sixteen 2-byte values.
+__device__ __forceinline__ uint2 quad_transpose_bf16(const float (&f)[4], int j) {
+  const uint32_t p0 = pack_bf16x2_hw(f[0], f[1]);  // rows 0, 1 of my column
+  const uint32_t p1 = pack_bf16x2_hw(f[2], f[3]);  // rows 2, 3
+  const bool odd = j & 1;
+  // lanes j, j^1: the even one gathers rows 0, 1 of both columns, the odd one
+  // rows 2, 3
+  const uint32_t got1 = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(odd ? p0 : p1), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  const uint32_t own = odd ? p1 : p0;
+  const uint32_t lo = odd ? got1 : own, hi = odd ? own : got1;  // lower, higher column
+  const uint32_t r0 = (lo & 0xffffu) | (hi << 16);              // first row of the pair, 2 columns
+  const uint32_t r1 = (lo >> 16) | (hi & 0xffff0000u);          // second row
+  // lanes j, j^2: swap halves so each lane holds one row of all 4 columns
+  const bool upper = j & 2;
+  const uint32_t got2 = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(upper ? r0 : r1), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  return upper ? make_uint2(got2, r1) : make_uint2(r0, got2);
+}
+
+// Row of the quad block that quad_transpose_bf16 leaves in lane j.
+__device__ __forceinline__ int quad_transpose_row(int j) { return (j & 1) * 2 + (j >> 1); }
+
 // SiLU for the bf16 epilogues: x * rcp(1 + 2^(-x log2 e)) on the hardware
 // exp2 and reciprocal (about 1 ulp each, well inside the bf16 rounding that
 // follows); x -> -inf gives -0, x -> +inf gives x, NaN stays NaN.

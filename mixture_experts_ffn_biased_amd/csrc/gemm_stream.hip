@@ -294,32 +294,50 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   // Every wave is done reading the ring before it is reused for the output.
   raw_barrier();
 
+  // Epilogue: each quad of lanes transposes its 4 x 4 blocks (rows 8a + b of
+  // four consecutive columns) so that a lane writes 4 columns of one row, 8
+  // bytes, into the staging slots; the 16-byte chunk index of a staged row is
+  // XOR-swizzled with row & 7 so the rows of a block land in different banks.
   const int row_lane = 4 * (lane >> 5);
+  const int jq = lane & 3;
+  const int rq = quad_transpose_row(jq);
+  const int cq = (lane & 31) & ~3;  // first of the quad's columns within a 32-column block
+  auto staged = [](int row, int col, int row_bytes) {
+    return row * row_bytes + (((col >> 3) ^ (row & 7)) << 4) + (col & 7) * 2;
+  };
   uint16_t *C = static_cast<uint16_t *>(shared ? g.C_shared : g.C_routed);
   if (DUAL) {
     // H tile: BM rows x 128 columns bf16 (256 bytes a row); rows 0..127 in
     // slot 0, rows 128..255 in slot 1.
-    uint16_t *Ht = reinterpret_cast<uint16_t *>(wm ? ring.s[1] : ring.s[0]);
+    unsigned char *Ht = wm ? ring.s[1] : ring.s[0];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       if (mi >= nmi) break;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = mi * 32 + 8 * (r >> 2) + row_lane + (r & 3);
-        const int col = wn * 32 + (lane & 31);
-        const float a1 = acc[mi][0][r];
-        Ht[row * 128 + col] = f32_to_bf16_hw((EPI == EPI_GELU_GLU ? gelu(a1) : silu_fast(a1)) * acc[mi][1][r]);
+      for (int a = 0; a < 4; ++a) {
+        float f[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float a1 = acc[mi][0][4 * a + b];
+          f[b] = (EPI == EPI_GELU_GLU ? gelu(a1) : silu_fast(a1)) * acc[mi][1][4 * a + b];
+        }
+        const int row = mi * 32 + 8 * a + row_lane + rq;
+        *reinterpret_cast<uint2 *>(Ht + staged(row, wn * 32 + cq, 256)) = quad_transpose_bf16(f, jq);
       }
     }
     __syncthreads();
-#pragma unroll 4
-    for (int j = 0; j < BM * 16 / NT; ++j) {
-      const int q = tid + NT * j;
-      const int row = q >> 4, ch = q & 15;
-      const uint16_t *H = reinterpret_cast<const uint16_t *>(row < 128 ? ring.s[0] : ring.s[1]);
-      if (row < tl.nrows)
-        *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
-            *reinterpret_cast<const uint4 *>(H + (row & 127) * 128 + ch * 8);
+    constexpr int RPS = BM < 128 ? BM : 128;  // rows staged in one slot
+    constexpr int RPP = NT / 16;              // rows per pass, 16 threads of 16 B a row
+#pragma unroll
+    for (int sl = 0; sl < BM / RPS; ++sl) {
+#pragma unroll
+      for (int j = 0; j < RPS / RPP; ++j) {
+        const int rl = j * RPP + (tid >> 4), ch = tid & 15;
+        const int row = sl * RPS + rl;
+        if (row < tl.nrows)
+          *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
+              *reinterpret_cast<const uint4 *>(ring.s[sl] + staged(rl, ch * 8, 256));
+      }
     }
     __syncthreads();
   } else {
@@ -337,18 +355,21 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       if (mi >= nmi) break;
-      uint16_t *Ot = reinterpret_cast<uint16_t *>(
-          wm ? (mi < 2 ? ring.s[2] : ring.s[3]) : (mi < 2 ? ring.s[0] : ring.s[1]));
+      unsigned char *Ot = wm ? (mi < 2 ? ring.s[2] : ring.s[3]) : (mi < 2 ? ring.s[0] : ring.s[1]);
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = (mi & 1) * 32 + 8 * (r >> 2) + row_lane + (r & 3);
-          const int col = wn * 64 + ni * 32 + (lane & 31);
-          float v = acc[mi][ni][r];
-          if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) v += bv[ni];
-          if (EPI == EPI_BIAS_GELU) v = gelu(v);
-          Ot[row * 256 + col] = f32_to_bf16_hw(v);
+        for (int a = 0; a < 4; ++a) {
+          float f[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            float v = acc[mi][ni][4 * a + b];
+            if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) v += bv[ni];
+            if (EPI == EPI_BIAS_GELU) v = gelu(v);
+            f[b] = v;
+          }
+          const int row = (mi & 1) * 32 + 8 * a + row_lane + rq;
+          *reinterpret_cast<uint2 *>(Ot + staged(row, wn * 64 + ni * 32 + cq, 512)) = quad_transpose_bf16(f, jq);
         }
     }
     __syncthreads();
@@ -364,7 +385,7 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
         const int row = sl * RPS + rl;
         if (row < tl.nrows)
           *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
-              *reinterpret_cast<const uint4 *>(ring.s[sl] + rl * 512 + ch * 16);
+              *reinterpret_cast<const uint4 *>(ring.s[sl] + staged(rl, ch * 8, 512));
       }
     }
     __syncthreads();
