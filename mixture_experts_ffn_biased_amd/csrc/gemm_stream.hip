@@ -32,6 +32,12 @@
 //    the same lane; the bf16 result goes through LDS to 16-byte stores.  The
 //    GELU MLP's gate_up is a single product like down (256 W1 rows a slab),
 //    with bias and GELU in the epilogue.
+//  * The prefill variant hands the intermediate H from the first product to
+//    the second tile-blocked: a tile's rows are stored K-slice by K-slice,
+//    each slice its nrows x 32 values contiguous (same buffer size as
+//    row-major).  The second product's token loads are then 16 rows x 64 B
+//    of one contiguous KiB instead of 16 separate half cache lines, which
+//    raise the global-to-LDS load rate a good part.
 //  * Weights are read either in their plain [rows][K] layout or packed once
 //    (moe_pack_weights) so that each stage's 16 KB weight tile is contiguous
 //    in memory in exactly the order it lands in LDS.
@@ -62,6 +68,23 @@ constexpr int a_bytes() { return V<VAR>::BM * SBK * 2; }
 template <int VAR>
 constexpr int stage_bytes() { return a_bytes<VAR>() + B_BYTES; }
 
+// Which product writes, and which reads, H in the tile-blocked layout: the
+// epilogue kind names the product (gated or GELU first product, then the
+// plain or biased second one); only the prefill variant blocks.
+template <int EPI, int VAR>
+constexpr bool writes_blocked() {
+  return VAR == 0 && (EPI == EPI_SILU_GLU || EPI == EPI_GELU_GLU || EPI == EPI_BIAS_GELU);
+}
+template <int EPI, int VAR>
+constexpr bool reads_blocked() {
+  return VAR == 0 && (EPI == EPI_PLAIN || EPI == EPI_BIAS);
+}
+// Element offset of H[row][col] of a tile (first row row0, nrows rows) whose
+// rows are `ld` values long, in the tile-blocked layout.
+__device__ __forceinline__ int64_t blocked_off(int64_t row0, int nrows, int ld, int row, int col) {
+  return row0 * ld + static_cast<int64_t>(col / SBK) * nrows * SBK + row * SBK + (col % SBK);
+}
+
 struct StreamArgs {
   const Tile *tiles;
   const int2 *items;        // per-XCD segments of {tile id, n-slab}
@@ -90,6 +113,7 @@ struct Ring {
 // no private array is ever demoted to memory).
 struct Ptrs {
   const uint16_t *a0, *a1;
+  int a_ks;  // token-operand elements from one K-slice to the next
   const uint16_t *b0, *b1, *b2, *b3;
   __device__ __forceinline__ const uint16_t *a(int i) const { return i == 0 ? a0 : a1; }
   __device__ __forceinline__ const uint16_t *b(int i) const {
@@ -138,7 +162,7 @@ __device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Pt
     const int koff = kt * SBK;
     if (VAR == 0) {
 #pragma unroll
-      for (int i = 0; i < V<VAR>::A_LOADS; ++i) dma16(p.a(i) + koff, st + (wave * 2 + i) * 1024);
+      for (int i = 0; i < V<VAR>::A_LOADS; ++i) dma16(p.a(i) + kt * p.a_ks, st + (wave * 2 + i) * 1024);
     } else {
       // 32 rows: each wave loads 8 rows with its first 32 lanes.
       if (lane < 32) dma16(p.a(0) + koff, st + wave * 512);
@@ -207,6 +231,7 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   const uint16_t *A = static_cast<const uint16_t *>(shared ? g.A_shared : g.A_routed);
   auto a_row = [&](int r) -> const uint16_t * {
     const int rr = r < tl.nrows ? r : 0;  // rows past the count read row 0 (never stored)
+    if (reads_blocked<EPI, VAR>()) return A + blocked_off(tl.row0, tl.nrows, K, rr, 0);
     int64_t arow;
     if (g.gather && !shared)
       arow = g.perm[tl.row0 + rr] / g.k;
@@ -219,6 +244,7 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   // 32 lanes); lane l lands in row +l/4, physical chunk l%4, which holds
   // logical k-chunk (l%4) ^ ((row>>2)&3).
   Ptrs p{};
+  p.a_ks = reads_blocked<EPI, VAR>() ? tl.nrows * SBK : SBK;
 #pragma unroll
   for (int i = 0; i < V<VAR>::A_LOADS; ++i) {
     const int r = VAR == 0 ? (wave * 2 + i) * 16 + (lane >> 2) : wave * 8 + ((lane & 31) >> 2);
@@ -327,16 +353,33 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
     }
     __syncthreads();
     constexpr int RPS = BM < 128 ? BM : 128;  // rows staged in one slot
-    constexpr int RPP = NT / 16;              // rows per pass, 16 threads of 16 B a row
+    if (writes_blocked<EPI, VAR>()) {
+      // One 32-column slice a pass: a wave writes 16 rows x 64 B, one
+      // contiguous KiB; the 8 lanes of a bank group read 8 different rows.
+      const int sub = lane >> 4;
 #pragma unroll
-    for (int sl = 0; sl < BM / RPS; ++sl) {
+      for (int sl = 0; sl < BM / RPS; ++sl) {
 #pragma unroll
-      for (int j = 0; j < RPS / RPP; ++j) {
-        const int rl = j * RPP + (tid >> 4), ch = tid & 15;
-        const int row = sl * RPS + rl;
-        if (row < tl.nrows)
-          *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
-              *reinterpret_cast<const uint4 *>(ring.s[sl] + staged(rl, ch * 8, 256));
+        for (int q = 0; q < 4; ++q) {
+          const int rl = wave * 16 + (lane & 15);
+          const int row = sl * RPS + rl;
+          if (row < tl.nrows)
+            *reinterpret_cast<uint4 *>(C + blocked_off(tl.row0, tl.nrows, N, row, n0 + q * SBK + sub * 8)) =
+                *reinterpret_cast<const uint4 *>(ring.s[sl] + staged(rl, q * SBK + sub * 8, 256));
+        }
+      }
+    } else {
+      constexpr int RPP = NT / 16;  // rows per pass, 16 threads of 16 B a row
+#pragma unroll
+      for (int sl = 0; sl < BM / RPS; ++sl) {
+#pragma unroll
+        for (int j = 0; j < RPS / RPP; ++j) {
+          const int rl = j * RPP + (tid >> 4), ch = tid & 15;
+          const int row = sl * RPS + rl;
+          if (row < tl.nrows)
+            *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
+                *reinterpret_cast<const uint4 *>(ring.s[sl] + staged(rl, ch * 8, 256));
+        }
       }
     }
     __syncthreads();
@@ -376,16 +419,34 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
     // Copy-out slot by slot (static slot index: a runtime choice among the
     // ring pointers would make the compiler keep them in memory).
     constexpr int RPS = BM < 64 ? BM : 64;  // rows staged in one slot
-    constexpr int RPP = NT / 32;            // rows per pass, 32 threads of 16 B a row
+    if (writes_blocked<EPI, VAR>()) {
+      // As in the gated case: a wave writes 16 rows of one 32-column slice;
+      // four waves cover a slot's 64 rows, the other four the next slice.
+      const int sub = lane >> 4;
+      const int rl = (wave & 3) * 16 + (lane & 15);
 #pragma unroll
-    for (int sl = 0; sl < BM / RPS; ++sl) {
+      for (int sl = 0; sl < BM / RPS; ++sl) {
 #pragma unroll
-      for (int j = 0; j < RPS / RPP; ++j) {
-        const int rl = j * RPP + (tid >> 5), ch = tid & 31;
-        const int row = sl * RPS + rl;
-        if (row < tl.nrows)
-          *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
-              *reinterpret_cast<const uint4 *>(ring.s[sl] + staged(rl, ch * 8, 512));
+        for (int j = 0; j < 4; ++j) {
+          const int q = 2 * j + (wave >> 2);
+          const int row = sl * RPS + rl;
+          if (row < tl.nrows)
+            *reinterpret_cast<uint4 *>(C + blocked_off(tl.row0, tl.nrows, N, row, n0 + q * SBK + sub * 8)) =
+                *reinterpret_cast<const uint4 *>(ring.s[sl] + staged(rl, q * SBK + sub * 8, 512));
+        }
+      }
+    } else {
+      constexpr int RPP = NT / 32;  // rows per pass, 32 threads of 16 B a row
+#pragma unroll
+      for (int sl = 0; sl < BM / RPS; ++sl) {
+#pragma unroll
+        for (int j = 0; j < RPS / RPP; ++j) {
+          const int rl = j * RPP + (tid >> 5), ch = tid & 31;
+          const int row = sl * RPS + rl;
+          if (row < tl.nrows)
+            *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
+                *reinterpret_cast<const uint4 *>(ring.s[sl] + staged(rl, ch * 8, 512));
+        }
       }
     }
     __syncthreads();
