@@ -45,6 +45,8 @@
 #include "pipeline.hpp"
 #include "plan.hpp"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -56,31 +58,40 @@ constexpr int B_STAGE_ELEMS = SBN * SBK;  // packed: elements per weight stage b
 template <int VAR>
 struct V;
 template <>
-struct V<0> {  // prefill
-  static constexpr int BM = 256, NT = 512, NSTAGE = 4, A_LOADS = 2, B_LOADS = 2;
+struct V<0> {  // prefill (stage ring: NSTAGE slots; pair ring: PA_LOADS token loads a pair)
+  static constexpr int BM = 256, NT = 512, NSTAGE = 4, A_LOADS = 2, B_LOADS = 2, PA_LOADS = 4;
 };
 template <>
 struct V<1> {  // decode
   static constexpr int BM = 32, NT = 256, NSTAGE = 8, A_LOADS = 1, B_LOADS = 4;
 };
+constexpr int SBKA = 64;                       // prefill: K of a token slot
+constexpr int A_SLOT_BYTES = 256 * SBKA * 2;   // 32 KiB
 template <int VAR>
 constexpr int a_bytes() { return V<VAR>::BM * SBK * 2; }
 template <int VAR>
 constexpr int stage_bytes() { return a_bytes<VAR>() + B_BYTES; }
 
-// Which product writes, and which reads, H in the tile-blocked layout: the
-// epilogue kind names the product (gated or GELU first product, then the
-// plain or biased second one); only the prefill variant blocks.
+// The epilogue kind names the product: the gated or GELU first product
+// (gathered token rows in, H out) or the plain or biased second one (H in).
+// In the prefill variant the first product runs the pair ring (whole cache
+// lines of the gathered rows) and writes H tile-blocked; the second reads
+// that layout through the stage ring, one contiguous KiB a load.
+template <int EPI, int VAR>
+constexpr bool pair_ring() {
+  return VAR == 0 && (EPI == EPI_SILU_GLU || EPI == EPI_GELU_GLU || EPI == EPI_BIAS_GELU);
+}
 template <int EPI, int VAR>
 constexpr bool writes_blocked() {
-  return VAR == 0 && (EPI == EPI_SILU_GLU || EPI == EPI_GELU_GLU || EPI == EPI_BIAS_GELU);
+  return pair_ring<EPI, VAR>();
 }
 template <int EPI, int VAR>
 constexpr bool reads_blocked() {
   return VAR == 0 && (EPI == EPI_PLAIN || EPI == EPI_BIAS);
 }
 // Element offset of H[row][col] of a tile (first row row0, nrows rows) whose
-// rows are `ld` values long, in the tile-blocked layout.
+// rows are `ld` values long, in the tile-blocked layout: K-slice by K-slice
+// (32 values), each slice's nrows x 32 values contiguous.
 __device__ __forceinline__ int64_t blocked_off(int64_t row0, int nrows, int ld, int row, int col) {
   return row0 * ld + static_cast<int64_t>(col / SBK) * nrows * SBK + row * SBK + (col % SBK);
 }
@@ -92,6 +103,7 @@ struct StreamArgs {
   const int32_t *xcd_cnt;   // [8] segment lengths
   int32_t *counters;        // [8] zero on entry
   const int32_t *perm;      // gate_up: position -> slot
+  int64_t a_rows;           // rows of the (ungathered) token matrix: T for gate_up
   int k;
   int E;
   const void *A_routed, *A_shared;
@@ -112,15 +124,17 @@ struct Ring {
 // DMA source pointers of one thread (scalar members, not arrays, so that
 // no private array is ever demoted to memory).
 struct Ptrs {
-  const uint16_t *a0, *a1;
-  int a_ks;  // token-operand elements from one K-slice to the next
+  const uint16_t *a0, *a1, *a2, *a3;
+  int a_ks;  // prefill: token-operand elements from one 64-wide K-slice to the next
   const uint16_t *b0, *b1, *b2, *b3;
-  __device__ __forceinline__ const uint16_t *a(int i) const { return i == 0 ? a0 : a1; }
+  __device__ __forceinline__ const uint16_t *a(int i) const {
+    return i == 0 ? a0 : (i == 1 ? a1 : (i == 2 ? a2 : a3));
+  }
   __device__ __forceinline__ const uint16_t *b(int i) const {
     return i == 0 ? b0 : (i == 1 ? b1 : (i == 2 ? b2 : b3));
   }
   __device__ __forceinline__ void set_a(int i, const uint16_t *v) {
-    if (i == 0) a0 = v; else a1 = v;
+    if (i == 0) a0 = v; else if (i == 1) a1 = v; else if (i == 2) a2 = v; else a3 = v;
   }
   __device__ __forceinline__ void set_b(int i, const uint16_t *v) {
     if (i == 0) b0 = v; else if (i == 1) b1 = v; else if (i == 2) b2 = v; else b3 = v;
@@ -148,9 +162,10 @@ struct Rem<NS, PS, R, R> {
   __device__ __forceinline__ static void run(const Ring<NS> &, int, Issue &, Compute &) {}
 };
 
-// The K loop of one item for a wave with NMI active 32-row blocks.  Every
-// wave issues the same loads and barriers whatever its NMI, so waves with
-// different row counts stay in step.
+// The stage ring's K loop (the decode variant, and the prefill variant's
+// second product): NS slots, each a whole stage (token rows and weight rows
+// of one K-slice of 32).  Every wave issues the same loads and barriers
+// whatever its NMI, so waves with different row counts stay in step.
 template <bool PACKED, int VAR, int NMI>
 __device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Ptrs &p, int KT,
                                       int wave, int lane, int wm, int wn, int fo0, int fo1,
@@ -212,8 +227,203 @@ __device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Pt
   Rem<NS, PS, NS, 0>::run(ring, G * NS, issue, compute);
 }
 
-template <int EPI, bool PACKED, int VAR>
-__device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const Ring<V<VAR>::NSTAGE> &ring) {
+// ---- prefill K loop ----------------------------------------------------------
+
+// Prefill DMA sources: buffer resources (scalar registers; stage offsets go
+// in the scalar offset) plus 32-bit per-lane byte offsets, so the K loop
+// does no per-lane address arithmetic.  Each resource spans exactly its
+// operand, so no load can leave it.
+struct PPtrs {
+  __amdgpu_buffer_rsrc_t ar;  // token operand: the token matrix
+  int astep;                  // bytes from one 64-wide K-slice to the next
+  uint32_t ao0, ao1, ao2, ao3;
+  __amdgpu_buffer_rsrc_t br0, br1;  // weight operand, per load
+  int bstep;                        // bytes from one stage to the next
+  uint32_t bo0, bo1;
+  __device__ __forceinline__ uint32_t ao(int j) const {
+    return j == 0 ? ao0 : (j == 1 ? ao1 : (j == 2 ? ao2 : ao3));
+  }
+  __device__ __forceinline__ void set_ao(int j, uint32_t v) {
+    if (j == 0) ao0 = v; else if (j == 1) ao1 = v; else if (j == 2) ao2 = v; else ao3 = v;
+  }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t br(int i) const { return i == 0 ? br0 : br1; }
+  __device__ __forceinline__ uint32_t bo(int i) const { return i == 0 ? bo0 : bo1; }
+};
+
+// Token load j of wave w fills rows (4w + j) * 8 + l/8 of a token slot, lane
+// l in physical chunk l%8, which holds logical chunk (l%8) ^ (row & 7).  A
+// weight load fills 16 rows of 64 B: lane l in row +l/4, physical chunk l%4,
+// holding logical chunk (l%4) ^ ((row>>2)&3).
+template <int EPI, bool PACKED>
+__device__ __forceinline__ PPtrs prefill_ptrs(const StreamArgs &g, const Tile &tl, bool shared, int slab_y, int N,
+                                              int K, int KT, int n0, int wave, int lane) {
+  constexpr bool DUAL = epi_dual(EPI);
+  PPtrs p{};
+  const char *A = static_cast<const char *>(shared ? g.A_shared : g.A_routed);
+  p.ar = buffer_rsrc(A, static_cast<uint32_t>(g.a_rows * K * 2));
+  p.astep = SBKA * 2;
+#pragma unroll
+  for (int j = 0; j < V<0>::PA_LOADS; ++j) {
+    const int r = (wave * V<0>::PA_LOADS + j) * 8 + (lane >> 3);
+    const int rr = r < tl.nrows ? r : 0;  // rows past the count read row 0 (never stored)
+    const uint32_t chunk = static_cast<uint32_t>(((lane & 7) ^ (r & 7)) * 16);
+    const int64_t arow = (g.gather && !shared) ? g.perm[tl.row0 + rr] / g.k : static_cast<int64_t>(tl.row0) + rr;
+    p.set_ao(j, static_cast<uint32_t>(arow * K * 2) + chunk);
+  }
+  if (PACKED) {
+    // The slab's stage blocks are contiguous: block kt at kt * B_STAGE_ELEMS,
+    // load i of wave w at (w * B_LOADS + i) KiB in the block, lane at 16 B.
+    const char *Bp = static_cast<const char *>(shared ? g.Bp_shared : g.Bp_routed);
+    const int nslab = DUAL ? N / (SBN / 2) : N / SBN;
+    const int64_t slab = (shared ? 0 : static_cast<int64_t>(tl.group) * nslab) + slab_y;
+    const uint32_t slab_bytes = static_cast<uint32_t>(KT * B_STAGE_ELEMS * 2);
+    p.br0 = p.br1 = buffer_rsrc(Bp + slab * slab_bytes, slab_bytes);
+    p.bo0 = static_cast<uint32_t>((wave * V<0>::B_LOADS + 0) * 1024 + lane * 16);
+    p.bo1 = p.bo0 + 1024;
+    p.bstep = B_STAGE_ELEMS * 2;
+  } else {
+    const char *B0 = static_cast<const char *>(shared ? g.B0_shared : g.B0_routed);
+    const char *B1 = static_cast<const char *>(shared ? g.B1_shared : g.B1_routed);
+    const int64_t es = static_cast<int64_t>(N) * K * 2;  // one expert's matrix
+    if (!shared) {
+      B0 += tl.group * es;
+      if (DUAL) B1 += tl.group * es;
+    }
+#pragma unroll
+    for (int i = 0; i < V<0>::B_LOADS; ++i) {
+      // rb: the load's first row (uniform); its 16 rows lie in one 32-row
+      // half of a wave column, so W1 or W3 is a per-load choice.
+      const int rb = (wave * V<0>::B_LOADS + i) * 16;
+      const int r = rb + (lane >> 2);
+      const uint32_t c = static_cast<uint32_t>((lane & 3) ^ ((r >> 2) & 3));
+      const char *base = B0;
+      int brow;
+      if (DUAL) {
+        // 64 rows per wave column: 32 of W1, then the same 32 of W3.
+        brow = n0 + (rb >> 6) * 32 + (rb & 31) + (lane >> 2);
+        if ((rb & 63) >= 32) base = B1;
+      } else {
+        brow = n0 + r;
+      }
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, static_cast<uint32_t>(es));
+      const uint32_t off = static_cast<uint32_t>(static_cast<int64_t>(brow) * K * 2) + c * 16;
+      if (i == 0) {
+        p.br0 = rs;
+        p.bo0 = off;
+      } else {
+        p.br1 = rs;
+        p.bo1 = off;
+      }
+    }
+    p.bstep = SBK * 2;
+  }
+  return p;
+}
+
+// Token slots hold 256 rows x 64 K values (128 B a row), so one 1 KiB load
+// covers 8 rows x 128 B, whole cache lines of the gathered token rows, where
+// 32-wide slices would cover 16 half lines; weight slots hold one stage, 256
+// rows x 32 K values, as in the decode ring.  Row r of a token slot keeps its
+// logical 16-byte chunk c in physical chunk c ^ (r & 7).
+struct PRing {
+  unsigned char *a0, *a1, *a2;
+  unsigned char *b0, *b1, *b2, *b3;
+};
+template <int I>
+__device__ __forceinline__ unsigned char *pa(const PRing &r) {
+  return I == 0 ? r.a0 : (I == 1 ? r.a1 : r.a2);
+}
+template <int I>
+__device__ __forceinline__ unsigned char *pb(const PRing &r) {
+  return I == 0 ? r.b0 : (I == 1 ? r.b1 : (I == 2 ? r.b2 : r.b3));
+}
+
+// Stages base + I .. base + 11 of one turn, statically unrolled: token slot
+// (I/2) % 3, weight slot I % 4 (base is a multiple of 12), so every slot
+// index is a constant.  Iteration t issues token pair t/2 + 2 when t is
+// even, then weight stage t + 3: loads that would lie past K go to a
+// zero-length buffer (they read zeros, touch no memory and land in a slot
+// no later stage reads), so every iteration issues the same loads, the
+// issue is never conditional, and the wait is the same 8 loads each time:
+// stage t's weights were the last load of iteration t-3 (after its token
+// pair), its token pair went out earlier still, and iterations t-2 and t-1
+// issued 4 + 2 + 2 loads.  The stage count is checked at run time, so the
+// last, partial turn runs the same code.
+// GUARD: the turn may end inside K (the last, partial turn); whole turns run
+// without the check, so their loop has a single back edge.
+template <int I, bool GUARD>
+struct PStep {
+  template <class IA, class IB, class C>
+  __device__ __forceinline__ static void run(const PRing &ring, int base, int KT, IA &ia, IB &ib, C &c) {
+    const int t = base + I;
+    if (GUARD && t >= KT) return;
+    wait_vmcnt<8>();
+    raw_barrier();
+    if (I % 2 == 0) ia(pa<(I / 2 + 2) % 3>(ring), t / 2 + 2, t + 4 < KT);
+    ib(pb<(I + 3) % 4>(ring), t + 3, t + 3 < KT);
+    c(pa<(I / 2) % 3>(ring), I & 1, pb<I % 4>(ring));
+    PStep<I + 1, GUARD>::run(ring, base, KT, ia, ib, c);
+  }
+};
+template <bool GUARD>
+struct PStep<12, GUARD> {
+  template <class IA, class IB, class C>
+  __device__ __forceinline__ static void run(const PRing &, int, int, IA &, IB &, C &) {}
+};
+
+// K loop of one prefill item for a wave with NMI active 32-row blocks (KT a
+// multiple of 4).  Every wave issues the same loads and barriers whatever its
+// NMI, so waves with different row counts stay in step.
+template <bool PACKED, int NMI>
+__device__ __forceinline__ void kloop_prefill(const PRing &ring, const PPtrs &p, int KT, int wave, int wm,
+                                              int wn, int xa, int fo0, int fo1, f32x16 (&acc)[4][2]) {
+  const __amdgpu_buffer_rsrc_t none = buffer_rsrc(nullptr, 0);
+  auto issue_a = [&](unsigned char *st, int q, bool real) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = real ? p.ar : none;
+#pragma unroll
+    for (int j = 0; j < V<0>::PA_LOADS; ++j) dma16_buf(r, p.ao(j), q * p.astep, st + (wave * V<0>::PA_LOADS + j) * 1024);
+  };
+  auto issue_b = [&](unsigned char *st, int kt, bool real) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < V<0>::B_LOADS; ++i)
+      dma16_buf(real ? p.br(i) : none, p.bo(i), kt * p.bstep, st + (wave * V<0>::B_LOADS + i) * 1024);
+  };
+  // half: which 32 of the token slot's 64 K values this stage multiplies.
+  auto compute = [&](const unsigned char *sta, int half, const unsigned char *stb) __attribute__((always_inline)) {
+    if (NMI == 0) return;
+    const unsigned char *sa = sta + wm * 128 * (SBKA * 2);
+    const unsigned char *sb = stb + wn * 64 * (SBK * 2);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int foa = xa ^ ((half * 4 + kk * 2) << 4);
+      const int fob = kk ? fo1 : fo0;
+      bf16x8 a[NMI > 0 ? NMI : 1], b[2];
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) a[mi] = *reinterpret_cast<const bf16x8 *>(sa + mi * 32 * (SBKA * 2) + foa);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) b[ni] = *reinterpret_cast<const bf16x8 *>(sb + ni * 2048 + fob);
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+  };
+  // Iterations -4 .. -1 of the pattern: pairs 0 and 1, stages 0 .. 2 (KT >= 4).
+  issue_a(ring.a0, 0, true);
+  issue_b(ring.b0, 0, true);
+  issue_a(ring.a1, 1, true);
+  issue_b(ring.b1, 1, true);
+  issue_b(ring.b2, 2, true);
+  const int G = KT / 12;
+  for (int j = 0; j < G; ++j) PStep<0, false>::run(ring, 12 * j, KT, issue_a, issue_b, compute);
+  if (12 * G < KT) PStep<0, true>::run(ring, 12 * G, KT, issue_a, issue_b, compute);
+  // The loads past K may still be landing in slots the epilogue stages in.
+  wait_vmcnt<0>();
+}
+
+template <int EPI, bool PACKED, int VAR, class RingT>
+__device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const RingT &ring) {
   constexpr int BM = V<VAR>::BM, NT = V<VAR>::NT;
   constexpr bool DUAL = epi_dual(EPI);
   const Tile tl = g.tiles[item.x];
@@ -228,67 +438,73 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = VAR == 0 ? wave >> 2 : 0, wn = VAR == 0 ? (wave & 3) : wave;
 
-  const uint16_t *A = static_cast<const uint16_t *>(shared ? g.A_shared : g.A_routed);
-  auto a_row = [&](int r) -> const uint16_t * {
-    const int rr = r < tl.nrows ? r : 0;  // rows past the count read row 0 (never stored)
-    if (reads_blocked<EPI, VAR>()) return A + blocked_off(tl.row0, tl.nrows, K, rr, 0);
-    int64_t arow;
-    if (g.gather && !shared)
-      arow = g.perm[tl.row0 + rr] / g.k;
-    else
-      arow = static_cast<int64_t>(tl.row0) + rr;
-    return A + arow * K;
-  };
-
-  // DMA sources.  A load fills 16 LDS rows (8 in the decode variant, first
-  // 32 lanes); lane l lands in row +l/4, physical chunk l%4, which holds
-  // logical k-chunk (l%4) ^ ((row>>2)&3).
+  // DMA sources: the pair ring's (PPtrs), or 64-bit pointers per lane for
+  // the stage ring.
+  constexpr bool PAIR = pair_ring<EPI, VAR>();
   Ptrs p{};
-  p.a_ks = reads_blocked<EPI, VAR>() ? tl.nrows * SBK : SBK;
-#pragma unroll
-  for (int i = 0; i < V<VAR>::A_LOADS; ++i) {
-    const int r = VAR == 0 ? (wave * 2 + i) * 16 + (lane >> 2) : wave * 8 + ((lane & 31) >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
-    p.set_a(i, a_row(r) + c * 8);
-  }
-  if (PACKED) {
-    // The slab's stage blocks are contiguous: block kt at kt * B_STAGE_ELEMS,
-    // load i of wave w at (w * B_LOADS + i) KiB in the block, lane at 16 B.
-    const uint16_t *Bp = static_cast<const uint16_t *>(shared ? g.Bp_shared : g.Bp_routed);
-    const int nslab = DUAL ? N / (SBN / 2) : N / SBN;
-    const int64_t slab = (shared ? 0 : static_cast<int64_t>(tl.group) * nslab) + item.y;
-    const uint16_t *blk = Bp + slab * KT * B_STAGE_ELEMS;
-#pragma unroll
-    for (int i = 0; i < V<VAR>::B_LOADS; ++i) p.set_b(i, blk + (wave * V<VAR>::B_LOADS + i) * 512 + lane * 8);
+  PPtrs pp{};
+  if constexpr (PAIR) {
+    pp = prefill_ptrs<EPI, PACKED>(g, tl, shared, item.y, N, K, KT, n0, wave, lane);
   } else {
-    const uint16_t *B0 = static_cast<const uint16_t *>(shared ? g.B0_shared : g.B0_routed);
-    const uint16_t *B1 = static_cast<const uint16_t *>(shared ? g.B1_shared : g.B1_routed);
-    if (!shared) {
-      const int64_t es = static_cast<int64_t>(N) * K;
-      B0 += tl.group * es;
-      if (DUAL) B1 += tl.group * es;
-    }
+    const uint16_t *A = static_cast<const uint16_t *>(shared ? g.A_shared : g.A_routed);
+    auto a_row = [&](int r) -> const uint16_t * {
+      const int rr = r < tl.nrows ? r : 0;  // rows past the count read row 0 (never stored)
+      if (reads_blocked<EPI, VAR>()) return A + blocked_off(tl.row0, tl.nrows, K, rr, 0);
+      const int64_t arow =
+          (g.gather && !shared) ? g.perm[tl.row0 + rr] / g.k : static_cast<int64_t>(tl.row0) + rr;
+      return A + arow * K;
+    };
+    // A token load fills 16 rows (8 in the decode variant, its first 32
+    // lanes) of 64 B: lane l in row +l/4, physical chunk l%4, holding logical
+    // chunk (l%4) ^ ((row>>2)&3).  Blocked H steps nrows * 32 values a stage.
+    p.a_ks = reads_blocked<EPI, VAR>() ? tl.nrows * SBK : SBK;
 #pragma unroll
-    for (int i = 0; i < V<VAR>::B_LOADS; ++i) {
-      const int r = (wave * V<VAR>::B_LOADS + i) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
-      int64_t brow;
-      const uint16_t *bsrc = B0;
-      if (DUAL) {
-        // 64 rows per wave column: 32 of W1, then the same 32 of W3.
-        const int q = r & 63;
-        brow = n0 + (r >> 6) * 32 + (q & 31);
-        if (q >= 32) bsrc = B1;
-      } else {
-        brow = n0 + r;
+    for (int i = 0; i < V<VAR>::A_LOADS; ++i) {
+      const int r = VAR == 0 ? (wave * 2 + i) * 16 + (lane >> 2) : wave * 8 + ((lane & 31) >> 2);
+      p.set_a(i, a_row(r) + ((lane & 3) ^ ((r >> 2) & 3)) * 8);
+    }
+    if (PACKED) {
+      // The slab's stage blocks are contiguous: block kt at kt * B_STAGE_ELEMS,
+      // load i of wave w at (w * B_LOADS + i) KiB in the block, lane at 16 B.
+      const uint16_t *Bp = static_cast<const uint16_t *>(shared ? g.Bp_shared : g.Bp_routed);
+      const int nslab = DUAL ? N / (SBN / 2) : N / SBN;
+      const int64_t slab = (shared ? 0 : static_cast<int64_t>(tl.group) * nslab) + item.y;
+      const uint16_t *blk = Bp + slab * KT * B_STAGE_ELEMS;
+#pragma unroll
+      for (int i = 0; i < V<VAR>::B_LOADS; ++i) p.set_b(i, blk + (wave * V<VAR>::B_LOADS + i) * 512 + lane * 8);
+    } else {
+      const uint16_t *B0 = static_cast<const uint16_t *>(shared ? g.B0_shared : g.B0_routed);
+      const uint16_t *B1 = static_cast<const uint16_t *>(shared ? g.B1_shared : g.B1_routed);
+      if (!shared) {
+        const int64_t es = static_cast<int64_t>(N) * K;
+        B0 += tl.group * es;
+        if (DUAL) B1 += tl.group * es;
       }
-      p.set_b(i, bsrc + brow * K + c * 8);
+#pragma unroll
+      for (int i = 0; i < V<VAR>::B_LOADS; ++i) {
+        const int r = (wave * V<VAR>::B_LOADS + i) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        int64_t brow;
+        const uint16_t *bsrc = B0;
+        if (DUAL) {
+          // 64 rows per wave column: 32 of W1, then the same 32 of W3.
+          const int q = r & 63;
+          brow = n0 + (r >> 6) * 32 + (q & 31);
+          if (q >= 32) bsrc = B1;
+        } else {
+          brow = n0 + r;
+        }
+        p.set_b(i, bsrc + brow * K + c * 8);
+      }
     }
   }
 
   const int sw = (lane >> 2) & 3;
   const int fo0 = (lane & 31) * 64 + (((0 + (lane >> 5)) ^ sw) << 4);
   const int fo1 = (lane & 31) * 64 + (((2 + (lane >> 5)) ^ sw) << 4);
+  // Prefill token fragment: row lane%32 (row & 7 == lane & 7), logical chunk
+  // 4 * half + 2 * kk + lane/32; the K loop XORs in the static part.
+  const int xa = (lane & 31) * (SBKA * 2) + (((lane >> 5) ^ (lane & 7)) << 4);
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -306,7 +522,15 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   // The previous item's stores and loads are complete before the ring refills.
   wait_vmcnt<0>();
   raw_barrier();
-  if (VAR == 0) {
+  if constexpr (PAIR) {
+    switch (nmi) {
+      case 0: kloop_prefill<PACKED, 0>(ring, pp, KT, wave, wm, wn, xa, fo0, fo1, acc); break;
+      case 1: kloop_prefill<PACKED, 1>(ring, pp, KT, wave, wm, wn, xa, fo0, fo1, acc); break;
+      case 2: kloop_prefill<PACKED, 2>(ring, pp, KT, wave, wm, wn, xa, fo0, fo1, acc); break;
+      case 3: kloop_prefill<PACKED, 3>(ring, pp, KT, wave, wm, wn, xa, fo0, fo1, acc); break;
+      default: kloop_prefill<PACKED, 4>(ring, pp, KT, wave, wm, wn, xa, fo0, fo1, acc); break;
+    }
+  } else if constexpr (VAR == 0) {
     switch (nmi) {
       case 0: kloop<PACKED, VAR, 0>(ring, p, KT, wave, lane, wm, wn, fo0, fo1, acc); break;
       case 1: kloop<PACKED, VAR, 1>(ring, p, KT, wave, lane, wm, wn, fo0, fo1, acc); break;
@@ -332,10 +556,51 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
     return row * row_bytes + (((col >> 3) ^ (row & 7)) << 4) + (col & 7) * 2;
   };
   uint16_t *C = static_cast<uint16_t *>(shared ? g.C_shared : g.C_routed);
+  // Tile-blocked copy-out of rows staged RS to a slot, 512 / 256 bytes a row
+  // (RB): a wave writes 16 rows x 64 B of one 32-column slice, one contiguous
+  // KiB; the 8 lanes of a bank group read 8 different rows.
+  const int bsub = lane >> 4;
+  auto copy_blocked = [&](const unsigned char *slot, int rf, auto rs, auto rb) __attribute__((always_inline)) {
+    constexpr int RS = decltype(rs)::value, RB = decltype(rb)::value;
+    constexpr int NSL = RB / (SBK * 2);  // 32-column slices in a staged row
+    constexpr int WPS = RS / 16;         // waves covering one slice of the slot
+    constexpr int SPP = 8 / WPS;         // slices per pass
+#pragma unroll
+    for (int j = 0; j < NSL / SPP; ++j) {
+      const int q = j * SPP + wave / WPS;
+      const int rl = (wave % WPS) * 16 + (lane & 15);
+      const int row = rf + rl;
+      if (row < tl.nrows)
+        *reinterpret_cast<uint4 *>(C + blocked_off(tl.row0, tl.nrows, N, row, n0 + q * SBK + bsub * 8)) =
+            *reinterpret_cast<const uint4 *>(slot + staged(rl, q * SBK + bsub * 8, RB));
+    }
+  };
+  // Row-major copy-out: TPR threads of 16 B a row.
+  auto copy_rows = [&](const unsigned char *slot, int rf, auto rs, auto rb) __attribute__((always_inline)) {
+    constexpr int RS = decltype(rs)::value, RB = decltype(rb)::value;
+    constexpr int TPR = RB / 16, RPP = NT / TPR;  // threads a row, rows a pass
+#pragma unroll
+    for (int j = 0; j < RS / RPP; ++j) {
+      const int rl = j * RPP + tid / TPR, ch = tid % TPR;
+      const int row = rf + rl;
+      if (row < tl.nrows)
+        *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
+            *reinterpret_cast<const uint4 *>(slot + staged(rl, ch * 8, RB));
+    }
+  };
+  using I32 = std::integral_constant<int, 32>;
+  using I64 = std::integral_constant<int, 64>;
+  using I128 = std::integral_constant<int, 128>;
+  using I256 = std::integral_constant<int, 256>;
+  using I512 = std::integral_constant<int, 512>;
   if (DUAL) {
-    // H tile: BM rows x 128 columns bf16 (256 bytes a row); rows 0..127 in
-    // slot 0, rows 128..255 in slot 1.
-    unsigned char *Ht = wm ? ring.s[1] : ring.s[0];
+    // H tile: BM rows x 128 columns bf16 (256 bytes a row), 128 rows a slot
+    // (pair ring: token slots 0 and 1; stage ring: slots 0 and 1).
+    unsigned char *Ht;
+    if constexpr (PAIR)
+      Ht = wm ? ring.a1 : ring.a0;
+    else
+      Ht = wm ? ring.s[1] : ring.s[0];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       if (mi >= nmi) break;
@@ -352,40 +617,19 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
       }
     }
     __syncthreads();
-    constexpr int RPS = BM < 128 ? BM : 128;  // rows staged in one slot
-    if (writes_blocked<EPI, VAR>()) {
-      // One 32-column slice a pass: a wave writes 16 rows x 64 B, one
-      // contiguous KiB; the 8 lanes of a bank group read 8 different rows.
-      const int sub = lane >> 4;
-#pragma unroll
-      for (int sl = 0; sl < BM / RPS; ++sl) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int rl = wave * 16 + (lane & 15);
-          const int row = sl * RPS + rl;
-          if (row < tl.nrows)
-            *reinterpret_cast<uint4 *>(C + blocked_off(tl.row0, tl.nrows, N, row, n0 + q * SBK + sub * 8)) =
-                *reinterpret_cast<const uint4 *>(ring.s[sl] + staged(rl, q * SBK + sub * 8, 256));
-        }
-      }
+    if constexpr (PAIR) {
+      copy_blocked(ring.a0, 0, I128{}, I256{});
+      copy_blocked(ring.a1, 128, I128{}, I256{});
     } else {
-      constexpr int RPP = NT / 16;  // rows per pass, 16 threads of 16 B a row
-#pragma unroll
-      for (int sl = 0; sl < BM / RPS; ++sl) {
-#pragma unroll
-        for (int j = 0; j < RPS / RPP; ++j) {
-          const int rl = j * RPP + (tid >> 4), ch = tid & 15;
-          const int row = sl * RPS + rl;
-          if (row < tl.nrows)
-            *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
-                *reinterpret_cast<const uint4 *>(ring.s[sl] + staged(rl, ch * 8, 256));
-        }
-      }
+      copy_rows(ring.s[0], 0, std::integral_constant<int, (BM < 128 ? BM : 128)>{}, I256{});
+      if (BM > 128) copy_rows(ring.s[1], 128, I128{}, I256{});
     }
     __syncthreads();
   } else {
-    // Output tile: BM x 256 bf16 (512 bytes a row); rows 64*s .. 64*s+63 in
-    // slot s (the decode tile's 32 rows all in slot 0).
+    // Output tile: BM x 256 bf16 (512 bytes a row).  Pair ring: 32-row
+    // blocks 0-1, 2-3 and 4-5 in token slots 0, 1 and 2 (64 rows each),
+    // blocks 6 and 7 in weight slots 0 and 1.  Stage ring: 64 rows a slot
+    // (the decode tile's 32 rows in slot 0).
     float bv[2] = {0.f, 0.f};
     if (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
       const uint16_t *bias = static_cast<const uint16_t *>(shared ? g.bias_shared : g.bias_routed);
@@ -398,7 +642,18 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       if (mi >= nmi) break;
-      unsigned char *Ot = wm ? (mi < 2 ? ring.s[2] : ring.s[3]) : (mi < 2 ? ring.s[0] : ring.s[1]);
+      unsigned char *Ot;
+      int rbase = (mi & 1) * 32;
+      if constexpr (PAIR) {
+        if (wm == 0) {
+          Ot = mi < 2 ? ring.a0 : ring.a1;
+        } else {
+          Ot = mi < 2 ? ring.a2 : (mi == 2 ? ring.b0 : ring.b1);
+          if (mi >= 2) rbase = 0;
+        }
+      } else {
+        Ot = wm ? (mi < 2 ? ring.s[2] : ring.s[3]) : (mi < 2 ? ring.s[0] : ring.s[1]);
+      }
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
@@ -411,53 +666,36 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
             if (EPI == EPI_BIAS_GELU) v = gelu(v);
             f[b] = v;
           }
-          const int row = (mi & 1) * 32 + 8 * a + row_lane + rq;
+          const int row = rbase + 8 * a + row_lane + rq;
           *reinterpret_cast<uint2 *>(Ot + staged(row, wn * 64 + ni * 32 + cq, 512)) = quad_transpose_bf16(f, jq);
         }
     }
     __syncthreads();
-    // Copy-out slot by slot (static slot index: a runtime choice among the
-    // ring pointers would make the compiler keep them in memory).
-    constexpr int RPS = BM < 64 ? BM : 64;  // rows staged in one slot
-    if (writes_blocked<EPI, VAR>()) {
-      // As in the gated case: a wave writes 16 rows of one 32-column slice;
-      // four waves cover a slot's 64 rows, the other four the next slice.
-      const int sub = lane >> 4;
-      const int rl = (wave & 3) * 16 + (lane & 15);
-#pragma unroll
-      for (int sl = 0; sl < BM / RPS; ++sl) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int q = 2 * j + (wave >> 2);
-          const int row = sl * RPS + rl;
-          if (row < tl.nrows)
-            *reinterpret_cast<uint4 *>(C + blocked_off(tl.row0, tl.nrows, N, row, n0 + q * SBK + sub * 8)) =
-                *reinterpret_cast<const uint4 *>(ring.s[sl] + staged(rl, q * SBK + sub * 8, 512));
-        }
-      }
+    // Copy-out region by region, each slot named statically (a runtime
+    // choice among the slot pointers would make the compiler keep them in
+    // memory).
+    if constexpr (PAIR) {
+      copy_blocked(ring.a0, 0, I64{}, I512{});
+      copy_blocked(ring.a1, 64, I64{}, I512{});
+      copy_blocked(ring.a2, 128, I64{}, I512{});
+      copy_blocked(ring.b0, 192, I32{}, I512{});
+      copy_blocked(ring.b1, 224, I32{}, I512{});
+    } else if constexpr (BM > 64) {
+      copy_rows(ring.s[0], 0, I64{}, I512{});
+      copy_rows(ring.s[1], 64, I64{}, I512{});
+      copy_rows(ring.s[2], 128, I64{}, I512{});
+      copy_rows(ring.s[3], 192, I64{}, I512{});
     } else {
-      constexpr int RPP = NT / 32;  // rows per pass, 32 threads of 16 B a row
-#pragma unroll
-      for (int sl = 0; sl < BM / RPS; ++sl) {
-#pragma unroll
-        for (int j = 0; j < RPS / RPP; ++j) {
-          const int rl = j * RPP + (tid >> 5), ch = tid & 31;
-          const int row = sl * RPS + rl;
-          if (row < tl.nrows)
-            *reinterpret_cast<uint4 *>(C + (static_cast<int64_t>(tl.row0) + row) * N + n0 + ch * 8) =
-                *reinterpret_cast<const uint4 *>(ring.s[sl] + staged(rl, ch * 8, 512));
-        }
-      }
+      copy_rows(ring.s[0], 0, std::integral_constant<int, BM>{}, I512{});
     }
     __syncthreads();
   }
 }
 
 // The ring is idle between items, so the fetched item index is broadcast
-// through the first word of slot 0.
-template <int EPI, bool PACKED, int VAR>
-__device__ __forceinline__ void item_loop(const StreamArgs &g, const Ring<V<VAR>::NSTAGE> &ring) {
-  int *item_sh = reinterpret_cast<int *>(ring.s[0]);
+// through the first word of a slot.
+template <int EPI, bool PACKED, int VAR, class RingT>
+__device__ __forceinline__ void item_loop(const StreamArgs &g, const RingT &ring, int *item_sh) {
   const int xcd = blockIdx.x & 7;
   for (int o = 0; o < 8; ++o) {
     const int x = (xcd + o) & 7;
@@ -466,7 +704,7 @@ __device__ __forceinline__ void item_loop(const StreamArgs &g, const Ring<V<VAR>
     for (;;) {
       if (threadIdx.x == 0) *item_sh = atomicAdd(&g.counters[x], 1);
       __syncthreads();
-      const int it = *item_sh;
+      const int it = __builtin_amdgcn_readfirstlane(*item_sh);
       __syncthreads();
       if (it >= cnt) break;
       run_item<EPI, PACKED, VAR>(g, g.items[off + it], ring);
@@ -478,14 +716,22 @@ __device__ __forceinline__ void item_loop(const StreamArgs &g, const Ring<V<VAR>
 // into one slot from the reads of another and adds no waits of its own.
 template <int EPI, bool PACKED>
 __global__ __launch_bounds__(512, 1) void gemm_stream_prefill(StreamArgs g) {
-  constexpr int SB = stage_bytes<0>();
-  __shared__ __attribute__((aligned(16))) unsigned char r0[SB], r1[SB], r2[SB], r3[SB];
-  Ring<4> ring;
-  ring.s[0] = r0;
-  ring.s[1] = r1;
-  ring.s[2] = r2;
-  ring.s[3] = r3;
-  item_loop<EPI, PACKED, 0>(g, ring);
+  if constexpr (pair_ring<EPI, 0>()) {
+    // 3 x 32 KiB token slots + 4 x 16 KiB weight slots: the whole 160 KiB.
+    __shared__ __attribute__((aligned(16))) unsigned char a0[A_SLOT_BYTES], a1[A_SLOT_BYTES], a2[A_SLOT_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char b0[B_BYTES], b1[B_BYTES], b2[B_BYTES], b3[B_BYTES];
+    PRing ring{a0, a1, a2, b0, b1, b2, b3};
+    item_loop<EPI, PACKED, 0>(g, ring, reinterpret_cast<int *>(a0));
+  } else {
+    constexpr int SB = stage_bytes<0>();
+    __shared__ __attribute__((aligned(16))) unsigned char r0[SB], r1[SB], r2[SB], r3[SB];
+    Ring<4> ring;
+    ring.s[0] = r0;
+    ring.s[1] = r1;
+    ring.s[2] = r2;
+    ring.s[3] = r3;
+    item_loop<EPI, PACKED, 0>(g, ring, reinterpret_cast<int *>(r0));
+  }
 }
 
 template <int EPI, bool PACKED>
@@ -502,7 +748,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_decode(StreamArgs g) {
   ring.s[5] = r5;
   ring.s[6] = r6;
   ring.s[7] = r7;
-  item_loop<EPI, PACKED, 1>(g, ring);
+  item_loop<EPI, PACKED, 1>(g, ring, reinterpret_cast<int *>(r0));
 }
 
 // ---- one-time weight packing -------------------------------------------------
@@ -774,6 +1020,7 @@ hipError_t launch_stream_gate_up(const Plan &p, const void *u, const Experts &x,
   StreamArgs a = base_args(p, 0);
   a.A_routed = u;
   a.A_shared = u;
+  a.a_rows = c.T;
   a.gather = 1;
   a.B0_routed = x.W1;
   a.B1_routed = dual ? x.W3 : nullptr;

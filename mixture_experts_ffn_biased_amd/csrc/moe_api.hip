@@ -54,6 +54,10 @@ static int choose_path(const moe_cfg &c, int kind) {
     if (c.F % 256 != 0 || c.F_shared % 256 != 0) return PATH_TILED;
     path = PATH_STREAM_DECODE;
   }
+  // The prefill variant addresses the token matrix and one expert's weight
+  // matrix with 32-bit byte offsets from their starts.
+  const int64_t f_max = c.F > c.F_shared ? c.F : c.F_shared;
+  if (path == PATH_STREAM && (c.T * c.d * 2 >= (1LL << 32) || f_max * c.d * 2 >= (1LL << 32))) return PATH_TILED;
   const int64_t m = stream_tile_m(path);
   const int64_t chunks = S / (2 * m) + c.E + c.T / (2 * m) + 4;
   if (chunks > stream_max_chunks()) return PATH_TILED;

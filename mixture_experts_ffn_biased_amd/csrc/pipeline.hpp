@@ -7,6 +7,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace moe {
 
@@ -31,6 +32,20 @@ __device__ __forceinline__ void raw_barrier() {
 // 16 bytes per lane from global memory into LDS at lds + lane * 16.
 __device__ __forceinline__ void dma16(const void *src, void *lds) {
   __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 16, 0, 0);
+}
+
+// Raw buffer resource over bytes [base, base + bytes) (bytes < 2^32):
+// offsets past the end read zeros instead of faulting.  Word 3 selects
+// 32-bit data, the usual setting for raw dword loads on gfx9 parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// The same 16-byte load into LDS through a buffer resource: the base and the
+// scalar offset stay in SGPRs, only the 32-bit lane offset is a VGPR.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, void *lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, static_cast<int>(voff), soff, 0, 0);
 }
 
 }  // namespace moe
