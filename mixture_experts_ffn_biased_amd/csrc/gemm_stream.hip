@@ -236,6 +236,7 @@ __device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Pt
 struct PPtrs {
   __amdgpu_buffer_rsrc_t ar;  // token operand: the token matrix
   int astep;                  // bytes from one 64-wide K-slice to the next
+  int alive;                  // bit j: token load j has a row of the tile (wave-uniform)
   uint32_t ao0, ao1, ao2, ao3;
   __amdgpu_buffer_rsrc_t br0, br1;  // weight operand, per load
   int bstep;                        // bytes from one stage to the next
@@ -262,6 +263,10 @@ __device__ __forceinline__ PPtrs prefill_ptrs(const StreamArgs &g, const Tile &t
   const char *A = static_cast<const char *>(shared ? g.A_shared : g.A_routed);
   p.ar = buffer_rsrc(A, static_cast<uint32_t>(g.a_rows * K * 2));
   p.astep = SBKA * 2;
+  p.alive = 0;
+#pragma unroll
+  for (int j = 0; j < V<0>::PA_LOADS; ++j)
+    if ((wave * V<0>::PA_LOADS + j) * 8 < tl.nrows) p.alive |= 1 << j;
 #pragma unroll
   for (int j = 0; j < V<0>::PA_LOADS; ++j) {
     const int r = (wave * V<0>::PA_LOADS + j) * 8 + (lane >> 3);
@@ -378,10 +383,13 @@ template <bool PACKED, int NMI>
 __device__ __forceinline__ void kloop_prefill(const PRing &ring, const PPtrs &p, int KT, int wave, int wm,
                                               int wn, int xa, int fo0, int fo1, f32x16 (&acc)[4][2]) {
   const __amdgpu_buffer_rsrc_t none = buffer_rsrc(nullptr, 0);
+  // A load whose 8 rows all lie past the tile's rows reads the zero-length
+  // resource too: the same count of loads, no memory traffic.
   auto issue_a = [&](unsigned char *st, int q, bool real) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = real ? p.ar : none;
 #pragma unroll
-    for (int j = 0; j < V<0>::PA_LOADS; ++j) dma16_buf(r, p.ao(j), q * p.astep, st + (wave * V<0>::PA_LOADS + j) * 1024);
+    for (int j = 0; j < V<0>::PA_LOADS; ++j)
+      dma16_buf(real && ((p.alive >> j) & 1) ? p.ar : none, p.ao(j), q * p.astep,
+                st + (wave * V<0>::PA_LOADS + j) * 1024);
   };
   auto issue_b = [&](unsigned char *st, int kt, bool real) __attribute__((always_inline)) {
 #pragma unroll

@@ -114,6 +114,10 @@ STREAM = {
                                              256, "sigmoid", 4, 2, 2.5, "bf16", "uniform"),
     "stream_many_tiles": Workload("stream_many_tiles", 2100, 256, 8, 3, 128, 128, "softmax", 1, 1,
                                   1.0, "bf16", "uniform"),
+    # d = 768: the first product's K loop is two whole 12-stage turns with no
+    # partial turn (d = 256 and 512 above end inside a turn).
+    "stream_d768_shared": Workload("stream_d768_shared", 900, 768, 8, 2, 256, 256, "sigmoid", 2, 1,
+                                   2.5, "bf16", "uniform"),
 }
 
 
