@@ -11,9 +11,26 @@
 #include "common.hpp"
 #include "plan.hpp"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
+// Widens 8 bf16 values (one 16-byte chunk) into acc += g * x, or acc = x.
+__device__ __forceinline__ void fma8(float (&acc)[8], float g, const uint4 &o) {
+  const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] = fmaf(g, bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu)), acc[2 * i]);
+    acc[2 * i + 1] = fmaf(g, bf16_to_f32(static_cast<uint16_t>(w[i] >> 16)), acc[2 * i + 1]);
+  }
+}
+
+// KB: the layer's k when it is one of the common values (every load of a
+// chunk then goes out before the first wait); 0 for any other k, which runs
+// in batches of 8.  HZ / HR: Z / R present.  The sum order is the same in
+// every case: Z, then j = 0 .. k-1, then R.
+template <int KB, bool HZ, bool HR>
 __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__ O,
                                                     const uint16_t *__restrict__ Z,
                                                     const int32_t *__restrict__ inv,
@@ -29,32 +46,32 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
     gw[threadIdx.x] = gates[t * k + threadIdx.x];
   }
   __syncthreads();
+  constexpr int NB = KB > 0 ? KB : 8;  // rows loaded together
   for (int c = threadIdx.x; c < nchunk; c += 256) {
+    const int64_t col = static_cast<int64_t>(c) * 8;
+    uint4 z = {0u, 0u, 0u, 0u}, r = {0u, 0u, 0u, 0u};
+    if (HZ) z = *reinterpret_cast<const uint4 *>(Z + t * d + col);
+    if (HR) r = *reinterpret_cast<const uint4 *>(R + t * d + col);
     float acc[8];
-    if (Z) {
-      const uint4 z = *reinterpret_cast<const uint4 *>(Z + t * d + c * 8);
+    {
       const uint32_t zw[4] = {z.x, z.y, z.z, z.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] = bf16_to_f32(static_cast<uint16_t>(zw[i] & 0xffffu));
         acc[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(zw[i] >> 16));
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     }
-    for (int j = 0; j < k; ++j) {
-      const uint4 o = *reinterpret_cast<const uint4 *>(O + static_cast<int64_t>(pos[j]) * d + c * 8);
-      const float g = gw[j];
-      const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+    const int kk = KB > 0 ? KB : k;
+    for (int j0 = 0; j0 < kk; j0 += NB) {
+      uint4 o[NB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(g, bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu)), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(g, bf16_to_f32(static_cast<uint16_t>(w[i] >> 16)), acc[2 * i + 1]);
-      }
+      for (int i = 0; i < NB; ++i)
+        if (KB > 0 || j0 + i < kk) o[i] = *reinterpret_cast<const uint4 *>(O + static_cast<int64_t>(pos[j0 + i]) * d + col);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (KB > 0 || j0 + i < kk) fma8(acc, gw[j0 + i], o[i]);
     }
-    if (R) {  // the block's residual, added last
-      const uint4 r = *reinterpret_cast<const uint4 *>(R + t * d + c * 8);
+    if (HR) {  // the block's residual, added last
       const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -67,7 +84,7 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
     out.y = pack_bf16x2(acc[2], acc[3]);
     out.z = pack_bf16x2(acc[4], acc[5]);
     out.w = pack_bf16x2(acc[6], acc[7]);
-    *reinterpret_cast<uint4 *>(y + t * d + c * 8) = out;
+    *reinterpret_cast<uint4 *>(y + t * d + col) = out;
   }
 }
 
@@ -111,11 +128,26 @@ hipError_t launch_combine(const Plan &p, const float *gates, const void *residua
   const moe_cfg &c = p.cfg;
   const void *Z = c.F_shared > 0 ? p.Z : nullptr;
   const dim3 grid(static_cast<unsigned>(c.T));
-  if (c.dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bf16, grid, dim3(256), 0, s, static_cast<const uint16_t *>(p.O),
+  if (c.dtype == MOE_BF16) {
+    const bool hz = Z != nullptr, hr = residual != nullptr;
+    auto pick = [&](auto kb) {
+      constexpr int KB = decltype(kb)::value;
+      return hz ? (hr ? combine_bf16<KB, true, true> : combine_bf16<KB, true, false>)
+                : (hr ? combine_bf16<KB, false, true> : combine_bf16<KB, false, false>);
+    };
+    auto kern = pick(std::integral_constant<int, 0>{});
+    switch (c.k) {
+      case 1: kern = pick(std::integral_constant<int, 1>{}); break;
+      case 2: kern = pick(std::integral_constant<int, 2>{}); break;
+      case 4: kern = pick(std::integral_constant<int, 4>{}); break;
+      case 6: kern = pick(std::integral_constant<int, 6>{}); break;
+      case 8: kern = pick(std::integral_constant<int, 8>{}); break;
+      default: break;
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, static_cast<const uint16_t *>(p.O),
                        static_cast<const uint16_t *>(Z), p.inv, gates, c.T, c.d, c.k,
                        static_cast<const uint16_t *>(residual), static_cast<uint16_t *>(y));
-  else
+  } else
     hipLaunchKernelGGL(combine_f32, grid, dim3(256), 0, s, static_cast<const float *>(p.O),
                        static_cast<const float *>(Z), p.inv, gates, c.T, c.d, c.k,
                        static_cast<const float *>(residual), static_cast<float *>(y));
