@@ -59,6 +59,8 @@ def parse():
                     help="skip the informational timings of the other layer shapes")
     ap.add_argument("--no-bodies", action="store_true",
                     help="skip the informational timings of the GEGLU and GELU-MLP expert bodies")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the decode layer replayed from a captured HIP graph")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB three times (a plain "
                          "copy kernel of known size, to scale hardware byte counters)")
@@ -164,6 +166,43 @@ def run_layer(w, inp, u, steps, warmup, torch, packed=None):
 
     ms, wall, stage_ms, calls = timed_steps(step, steps, warmup, torch)
     return ms, wall, stage_ms, idx
+
+
+def graph_ms(w, inp, u, packed, steps, torch):
+    """Average time of one layer call replayed from a captured HIP graph (the
+    same kernels without the per-call launch work)."""
+    import mixture_experts_ffn_biased_amd as moe
+    cfg = moe.MoeConfig.from_workload(w)
+    dev = u.device
+    y = torch.empty((w.T, w.d), dtype=u.dtype, device=dev)
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    gates = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    ws = moe.alloc_workspace(cfg, dev)
+
+    def step():
+        moe.moe_layer_forward_packed(u, inp["W_router"], inp["bias"], packed, cfg=cfg, y=y, topk_idx=idx,
+                                     gates=gates, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def layer_record(w, ms, stage_ms, hit, path):
@@ -459,6 +498,11 @@ def main():
             "roofline": roofline("gemm_stream_decode<gate_up>", gu_flops_d, gate_up_bytes(wd, hit),
                                  dstage[GATE_UP], stored_traffic(f"gate_up_{wd.name}")),
         }
+        if packed is not None and not args.no_graph:
+            gms = graph_ms(wd, inp, ud, packed, args.decode_steps, torch)
+            result["decode"]["graph_replay"] = {
+                "ms_per_step": round(gms, 4), "layer_GBps": round(layer_bytes / (gms * 1e-3) / 1e9, 1),
+                "layer_hbm_frac": round(layer_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
     if packed is not None and not args.no_plain:
         # the same layer with the weights in their plain layout, for reference
