@@ -15,29 +15,32 @@
 //    expert's token rows and weight slabs in that XCD's L2, and each weight
 //    byte is fetched from HBM about once.  A workgroup whose list is empty
 //    takes items from the other XCDs' lists.
-//  * Each stage is a K-slice of 32: the tile's token rows and 256 weight rows,
-//    staged by direct global-to-LDS 16-byte loads (global_load_lds_dwordx4)
-//    through a ring of LDS slots; all but one slot are in flight while one is
-//    multiplied; no VGPR staging.
+//  * Each stage is a K-slice of 32 of the tile's token rows and 256 weight
+//    rows, staged by direct global-to-LDS 16-byte loads into rings of
+//    separate LDS slots; three stages are in flight while one is multiplied;
+//    no VGPR staging.
 //  * Prefill variant: 256-row tiles, 8 waves in a 2x4 grid (two per SIMD, one
 //    from each row half), each 128 x 64 of v_mfma_f32_32x32x16_bf16 with fp32
-//    accumulators, a 4-slot ring (3 stages, 96 KB, in flight).  A wave multiplies only
-//    the 32-row blocks that hold rows of the tile (its K loop is specialised
-//    on that count), so a SIMD's MFMA work follows the tile's row count.
+//    accumulators.  A wave multiplies only the 32-row blocks that hold rows
+//    of the tile (its K loop is specialised on that count), so a SIMD's MFMA
+//    work follows the tile's row count.
+//    - First product (gathered token rows): the pair ring.  Token slots hold
+//      two stages (64 K values, 128 B a row), so a 1 KiB load covers 8 rows
+//      x 128 B, whole cache lines of the gathered rows; 3 token slots and 4
+//      weight slots fill the 160 KiB of LDS.  Loads go through buffer
+//      resources, so the K loop adds only scalar offsets.
+//    - Second product: the stage ring (4 slots of 32 KiB) over H, which the
+//      first product writes tile-blocked: a tile's rows K-slice by K-slice,
+//      each slice's nrows x 32 values contiguous (same size as row-major),
+//      so each 16-row token load is one contiguous KiB.
 //  * Decode variant (few rows per expert): 32-row tiles, 4 waves each 32 x 64,
-//    an 8-slot ring (7 x 16 KB of weights in flight): a weight stream with a
-//    small MFMA on the side.
+//    an 8-slot stage ring (7 x 16 KB of weights in flight): a weight stream
+//    with a small MFMA on the side.
 //  * gate_up of the gated bodies: each wave column's 64 weight rows are 32
 //    rows of W1 then the same 32 of W3, so act(x W1^T) * (x W3^T) meets in
 //    the same lane; the bf16 result goes through LDS to 16-byte stores.  The
 //    GELU MLP's gate_up is a single product like down (256 W1 rows a slab),
 //    with bias and GELU in the epilogue.
-//  * The prefill variant hands the intermediate H from the first product to
-//    the second tile-blocked: a tile's rows are stored K-slice by K-slice,
-//    each slice its nrows x 32 values contiguous (same buffer size as
-//    row-major).  The second product's token loads are then 16 rows x 64 B
-//    of one contiguous KiB instead of 16 separate half cache lines, which
-//    raise the global-to-LDS load rate a good part.
 //  * Weights are read either in their plain [rows][K] layout or packed once
 //    (moe_pack_weights) so that each stage's 16 KB weight tile is contiguous
 //    in memory in exactly the order it lands in LDS.
@@ -121,20 +124,18 @@ struct Ring {
   unsigned char *s[NS];
 };
 
-// DMA source pointers of one thread (scalar members, not arrays, so that
-// no private array is ever demoted to memory).
+// Stage-ring DMA source pointers of one thread (scalar members, not arrays,
+// so that no private array is ever demoted to memory).
 struct Ptrs {
-  const uint16_t *a0, *a1, *a2, *a3;
-  int a_ks;  // prefill: token-operand elements from one 64-wide K-slice to the next
+  const uint16_t *a0, *a1;
+  int a_ks;  // token-operand elements from one stage to the next
   const uint16_t *b0, *b1, *b2, *b3;
-  __device__ __forceinline__ const uint16_t *a(int i) const {
-    return i == 0 ? a0 : (i == 1 ? a1 : (i == 2 ? a2 : a3));
-  }
+  __device__ __forceinline__ const uint16_t *a(int i) const { return i == 0 ? a0 : a1; }
   __device__ __forceinline__ const uint16_t *b(int i) const {
     return i == 0 ? b0 : (i == 1 ? b1 : (i == 2 ? b2 : b3));
   }
   __device__ __forceinline__ void set_a(int i, const uint16_t *v) {
-    if (i == 0) a0 = v; else if (i == 1) a1 = v; else if (i == 2) a2 = v; else a3 = v;
+    if (i == 0) a0 = v; else a1 = v;
   }
   __device__ __forceinline__ void set_b(int i, const uint16_t *v) {
     if (i == 0) b0 = v; else if (i == 1) b1 = v; else if (i == 2) b2 = v; else b3 = v;
@@ -328,7 +329,7 @@ __device__ __forceinline__ PPtrs prefill_ptrs(const StreamArgs &g, const Tile &t
 // Token slots hold 256 rows x 64 K values (128 B a row), so one 1 KiB load
 // covers 8 rows x 128 B, whole cache lines of the gathered token rows, where
 // 32-wide slices would cover 16 half lines; weight slots hold one stage, 256
-// rows x 32 K values, as in the decode ring.  Row r of a token slot keeps its
+// rows x 32 K values, as in the stage ring.  Row r of a token slot keeps its
 // logical 16-byte chunk c in physical chunk c ^ (r & 7).
 struct PRing {
   unsigned char *a0, *a1, *a2;
@@ -352,10 +353,9 @@ __device__ __forceinline__ unsigned char *pb(const PRing &r) {
 // issue is never conditional, and the wait is the same 8 loads each time:
 // stage t's weights were the last load of iteration t-3 (after its token
 // pair), its token pair went out earlier still, and iterations t-2 and t-1
-// issued 4 + 2 + 2 loads.  The stage count is checked at run time, so the
-// last, partial turn runs the same code.
-// GUARD: the turn may end inside K (the last, partial turn); whole turns run
-// without the check, so their loop has a single back edge.
+// issued 4 + 2 + 2 loads.  Whole turns run without a stage-count check, so
+// their loop has a single back edge; the last, partial turn (GUARD) checks
+// the count and otherwise runs the same code.
 template <int I, bool GUARD>
 struct PStep {
   template <class IA, class IB, class C>
@@ -376,8 +376,8 @@ struct PStep<12, GUARD> {
   __device__ __forceinline__ static void run(const PRing &, int, int, IA &, IB &, C &) {}
 };
 
-// K loop of one prefill item for a wave with NMI active 32-row blocks (KT a
-// multiple of 4).  Every wave issues the same loads and barriers whatever its
+// K loop of one first-product prefill item (pair ring) for a wave with NMI
+// active 32-row blocks (KT a multiple of 4).  Every wave issues the same loads and barriers whatever its
 // NMI, so waves with different row counts stay in step.
 template <bool PACKED, int NMI>
 __device__ __forceinline__ void kloop_prefill(const PRing &ring, const PPtrs &p, int KT, int wave, int wm,
