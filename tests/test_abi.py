@@ -99,6 +99,14 @@ def test_gemm_path_selection():
     assert moe.moe_plan_describe(cfg(T=8, n_groups=1, topk_groups=1))[0] == "tiled"
 
 
+def test_prefill_stream_needs_a_token_matrix_below_4_gib():
+    # the prefill streaming kernels address u with 32-bit byte offsets: T * d * 2 < 2^32
+    big = dict(d=32768, E=8, k=2, F=256, n_groups=1, topk_groups=1)
+    assert 65535 * 32768 * 2 < 2 ** 32 <= 65536 * 32768 * 2
+    assert moe.moe_plan_describe(cfg(T=65535, **big))[0] == "stream"
+    assert moe.moe_plan_describe(cfg(T=65536, **big))[0] == "tiled"
+
+
 def test_packed_weight_size_is_the_weight_bytes():
     for name in ("mixtral_e8_top2", "dsv3_prefill", "dsv3_decode", "skewed_e128_top8"):
         w = WORKLOADS[name]
