@@ -1,6 +1,6 @@
 // Helpers for gfx950 kernels that stage tiles through LDS with direct
-// global-to-LDS loads (global_load_lds_dwordx4) in a ring of separate
-// __shared__ slots.  The wait counts are explicit: a stage is complete once
+// global-to-LDS loads (global_load_lds_dwordx4, or buffer_load_dwordx4 ...
+// lds through a buffer resource) in a ring of separate __shared__ slots.  The wait counts are explicit: a stage is complete once
 // at most the loads issued after it are outstanding (loads complete in
 // order), and the barrier is a bare s_barrier, which does not wait for the
 // in-flight LDS loads the way __syncthreads() does.
