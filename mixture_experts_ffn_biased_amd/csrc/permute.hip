@@ -50,9 +50,20 @@ __global__ __launch_bounds__(256) void perm_scan(
     int32_t *__restrict__ offsets, Tile *__restrict__ tiles, int32_t *__restrict__ tile_count) {
   __shared__ int buf[256];
   const int e = threadIdx.x;
+  // The per-block counts are read 16 at a time, so their loads overlap.
+  constexpr int U = 16;
   int c = 0;
-  if (e < E)
-    for (int b = 0; b < nblk; ++b) c += blk_counts[static_cast<int64_t>(b) * E + e];
+  if (e < E) {
+    int b = 0;
+    for (; b + U <= nblk; b += U) {
+      int v[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) v[i] = blk_counts[static_cast<int64_t>(b + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < U; ++i) c += v[i];
+    }
+    for (; b < nblk; ++b) c += blk_counts[static_cast<int64_t>(b) * E + e];
+  }
   const int nt = e < E ? (c + tile_m - 1) / tile_m : 0;
   int total_slots, total_tiles;
   const int off = exclusive_scan_256(e < E ? c : 0, buf, &total_slots);
@@ -61,7 +72,18 @@ __global__ __launch_bounds__(256) void perm_scan(
     counts[e] = c;
     offsets[e] = off;
     int run = off;
-    for (int b = 0; b < nblk; ++b) {
+    int b = 0;
+    for (; b + U <= nblk; b += U) {
+      int v[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) v[i] = blk_counts[static_cast<int64_t>(b + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        blk_base[static_cast<int64_t>(b + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+    for (; b < nblk; ++b) {
       blk_base[static_cast<int64_t>(b) * E + e] = run;
       run += blk_counts[static_cast<int64_t>(b) * E + e];
     }
@@ -86,34 +108,46 @@ __global__ __launch_bounds__(256) void perm_scan(
   if (e == 0) *tile_count = total_tiles + ns;
 }
 
-// Stable scatter: a block re-reads its chunk in rounds of 256 slots; a slot's
-// rank among equal experts earlier in its round plus the running count of
-// that expert gives its position.
+// Stable scatter: a block walks its chunk in rounds of 256 slots (4 waves of
+// 64).  A slot's position is the running count of its expert, plus the
+// slots of that expert in the earlier waves of the round, plus its rank
+// among the lanes of its own wave holding the same expert.  The lanes with
+// the same expert are found with one ballot per bit of the expert index.
 __global__ __launch_bounds__(256) void perm_scatter(const int32_t *__restrict__ idx, int64_t S, int E,
                                                     const int32_t *__restrict__ blk_base,
                                                     int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+  static_assert(kMaxExperts <= 256, "expert index in 8 bits");
   __shared__ int run[kMaxExperts];
-  __shared__ int ex[256];
-  const int tid = threadIdx.x;
+  __shared__ int wcnt[4][kMaxExperts];  // slots of each expert in each wave of the round
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += 256) run[e] = blk_base[blockIdx.x * static_cast<int64_t>(E) + e];
   const int64_t s0 = static_cast<int64_t>(blockIdx.x) * kPermChunk;
   const int64_t s1 = s0 + kPermChunk < S ? s0 + kPermChunk : S;
-  __syncthreads();
+  const uint64_t lower = (1ull << lane) - 1;
   for (int64_t base = s0; base < s1; base += 256) {
+    for (int i = tid; i < 4 * kMaxExperts; i += 256) (&wcnt[0][0])[i] = 0;
     const int64_t s = base + tid;
     const int e = s < s1 ? idx[s] : -1;
-    ex[tid] = e;
+    uint64_t same = __ballot(e >= 0);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool on = (e >> bit) & 1;
+      const uint64_t b = __ballot(on);
+      same &= on ? b : ~b;
+    }
+    const int rank = __popcll(same & lower);
+    __syncthreads();  // wcnt cleared, run up to date
+    if (e >= 0 && rank == 0) wcnt[wave][e] = __popcll(same);
     __syncthreads();
     if (e >= 0) {
-      int r = 0;
-      for (int j = 0; j < tid; ++j) r += ex[j] == e;
-      const int pos = run[e] + r;
+      int pos = run[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
       perm[pos] = static_cast<int32_t>(s);
       inv[s] = pos;
     }
     __syncthreads();
-    if (e >= 0) atomicAdd(&run[e], 1);
-    __syncthreads();
+    for (int ee = tid; ee < E; ee += 256) run[ee] += wcnt[0][ee] + wcnt[1][ee] + wcnt[2][ee] + wcnt[3][ee];
+    __syncthreads();  // wcnt is read above before the next round clears it
   }
 }
 
