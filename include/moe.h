@@ -138,7 +138,9 @@ moe_status moe_layer_forward(const void *u, const void *W_router, const float *b
  * moe_layer_forward_packed: moe_layer_forward with the packed buffer in
  *   place of W1, W3, W2 and shared (the shared expert is used iff
  *   cfg->F_shared > 0).  Returns MOE_ERR_SHAPE when cfg cannot be packed or
- *   T is too large for the streaming schedule.
+ *   is beyond the streaming kernels (moe_plan_describe then reports the
+ *   tiled kernels): T too large for the streaming schedule, or a token
+ *   matrix u of 4 GiB or more in the prefill variant.
  */
 size_t moe_packed_weights_bytes(const moe_cfg *cfg);
 moe_status moe_pack_weights(const moe_cfg *cfg, const void *W1, const void *W3, const void *W2,
@@ -300,8 +302,10 @@ moe_status moe_balance_update(const int32_t *topk_idx, int64_t T, int32_t k, int
  * GPU call): *gemm_path = 0 for the tiled kernels (any size, fp32 or bf16),
  * 1 for the persistent weight-streaming kernels with 256-row tiles (bf16,
  * d % 256 == 0, F % 128 == 0, F_shared % 128 == 0, at least 64 routed rows
- * per expert on average), 2 for their decode variant with 32-row tiles
- * (fewer rows per expert; also F % 256 == 0, F_shared % 256 == 0);
+ * per expert on average, T * d * 2 and max(F, F_shared) * d * 2 below 2^32
+ * bytes, which they address with 32-bit offsets), 2 for their decode variant
+ * with 32-row tiles (fewer rows per expert; also F % 256 == 0,
+ * F_shared % 256 == 0); both also need T within the streaming schedule;
  * *tile_rows = rows per GEMM tile.  Either pointer may be NULL.
  */
 moe_status moe_plan_describe(const moe_cfg *cfg, int32_t *gemm_path, int32_t *tile_rows);

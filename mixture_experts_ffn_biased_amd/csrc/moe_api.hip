@@ -376,7 +376,7 @@ moe_status moe_layer_forward_packed_ex(const void *u, const void *W_router, cons
   Plan p;
   st = check_forward(u, W_router, cfg, x.kind, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
-  if (p.path == PATH_TILED) return MOE_ERR_SHAPE;  // too many tiles for the streaming schedule
+  if (p.path == PATH_TILED) return MOE_ERR_SHAPE;  // beyond the streaming kernels' limits
   const PackedView pk = packed_view(*cfg, x.kind, packed);
   return run_layer(p, u, W_router, bias, x, &pk, y, topk_idx, gates, static_cast<hipStream_t>(stream));
 }
@@ -423,7 +423,7 @@ moe_status moe_layer_forward_packed(const void *u, const void *W_router, const f
   Plan p;
   st = check_forward(u, W_router, cfg, MOE_EXPERT_SWIGLU, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
-  if (p.path == PATH_TILED) return MOE_ERR_SHAPE;  // too many tiles for the streaming schedule
+  if (p.path == PATH_TILED) return MOE_ERR_SHAPE;  // beyond the streaming kernels' limits
   const PackedView pk = packed_view(*cfg, MOE_EXPERT_SWIGLU, packed);
   // The shared expert is present iff F_shared > 0 (the kernels read pk).
   return run_layer(p, u, W_router, bias, swiglu_experts(nullptr, nullptr, nullptr, nullptr), &pk, y, topk_idx,
