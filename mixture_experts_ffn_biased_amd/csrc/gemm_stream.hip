@@ -124,11 +124,18 @@ struct Ring {
   unsigned char *s[NS];
 };
 
-// Stage-ring DMA source pointers of one thread (scalar members, not arrays,
-// so that no private array is ever demoted to memory).
+// Stage-ring DMA sources of one thread (scalar members, not arrays, so that
+// no private array is ever demoted to memory).  The prefill variant (second
+// product) reads its token operand, the tile's block of H, through a buffer
+// resource: ar, lane offsets ao0/ao1, bytes a_ks from one stage to the next;
+// the decode variant through the pointer a0.
 struct Ptrs {
   const uint16_t *a0, *a1;
-  int a_ks;  // token-operand elements from one stage to the next
+  int a_ks;   // token-operand elements (decode) or bytes (prefill) from one stage to the next
+  __amdgpu_buffer_rsrc_t ar;
+  uint32_t ao0, ao1;
+  int alive;  // bit i: token load i has a row of the tile (wave-uniform)
+  __device__ __forceinline__ uint32_t ao(int i) const { return i == 0 ? ao0 : ao1; }
   const uint16_t *b0, *b1, *b2, *b3;
   __device__ __forceinline__ const uint16_t *a(int i) const { return i == 0 ? a0 : a1; }
   __device__ __forceinline__ const uint16_t *b(int i) const {
@@ -177,8 +184,12 @@ __device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Pt
   auto issue = [&](unsigned char *st, int kt) __attribute__((always_inline)) {
     const int koff = kt * SBK;
     if (VAR == 0) {
+      // A load whose 16 rows all lie past the tile's rows reads the
+      // zero-length resource: the same count of loads, no memory traffic.
 #pragma unroll
-      for (int i = 0; i < V<VAR>::A_LOADS; ++i) dma16(p.a(i) + kt * p.a_ks, st + (wave * 2 + i) * 1024);
+      for (int i = 0; i < V<VAR>::A_LOADS; ++i)
+        dma16_buf(((p.alive >> i) & 1) ? p.ar : buffer_rsrc(nullptr, 0), p.ao(i), kt * p.a_ks,
+                  st + (wave * 2 + i) * 1024);
     } else {
       // 32 rows: each wave loads 8 rows with its first 32 lanes.
       if (lane < 32) dma16(p.a(0) + koff, st + wave * 512);
@@ -464,12 +475,25 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
     };
     // A token load fills 16 rows (8 in the decode variant, its first 32
     // lanes) of 64 B: lane l in row +l/4, physical chunk l%4, holding logical
-    // chunk (l%4) ^ ((row>>2)&3).  Blocked H steps nrows * 32 values a stage.
-    p.a_ks = reads_blocked<EPI, VAR>() ? tl.nrows * SBK : SBK;
+    // chunk (l%4) ^ ((row>>2)&3).
+    if constexpr (VAR == 0) {
+      static_assert(reads_blocked<EPI, VAR>(), "the prefill stage ring reads tile-blocked H");
+      // The tile's block of H: stage kt at kt * nrows * 64 bytes, row r at r * 64.
+      p.ar = buffer_rsrc(A + static_cast<int64_t>(tl.row0) * K, static_cast<uint32_t>(tl.nrows * K * 2));
+      p.a_ks = tl.nrows * SBK * 2;
+      p.alive = 0;
 #pragma unroll
-    for (int i = 0; i < V<VAR>::A_LOADS; ++i) {
-      const int r = VAR == 0 ? (wave * 2 + i) * 16 + (lane >> 2) : wave * 8 + ((lane & 31) >> 2);
-      p.set_a(i, a_row(r) + ((lane & 3) ^ ((r >> 2) & 3)) * 8);
+      for (int i = 0; i < V<VAR>::A_LOADS; ++i) {
+        const int r = (wave * 2 + i) * 16 + (lane >> 2);
+        const int rr = r < tl.nrows ? r : 0;  // rows past the count read row 0 (never stored)
+        const uint32_t off = static_cast<uint32_t>(rr * SBK * 2 + (((lane & 3) ^ ((r >> 2) & 3)) << 4));
+        if (i == 0) p.ao0 = off; else p.ao1 = off;
+        if ((wave * 2 + i) * 16 < tl.nrows) p.alive |= 1 << i;
+      }
+    } else {
+      p.a_ks = SBK;
+      const int r = wave * 8 + ((lane & 31) >> 2);
+      p.set_a(0, a_row(r) + ((lane & 3) ^ ((r >> 2) & 3)) * 8);
     }
     if (PACKED) {
       // The slab's stage blocks are contiguous: block kt at kt * B_STAGE_ELEMS,
