@@ -135,7 +135,13 @@ struct Ptrs {
   __amdgpu_buffer_rsrc_t ar;
   uint32_t ao0, ao1;
   int alive;  // bit i: token load i has a row of the tile (wave-uniform)
+  // Prefill weight operand: a buffer resource over the packed slab or the
+  // expert's matrix, lane offsets bo0/bo1, bytes b_ks from one stage to the next.
+  __amdgpu_buffer_rsrc_t br;
+  uint32_t bo0, bo1;
+  int b_ks;
   __device__ __forceinline__ uint32_t ao(int i) const { return i == 0 ? ao0 : ao1; }
+  __device__ __forceinline__ uint32_t bo(int i) const { return i == 0 ? bo0 : bo1; }
   const uint16_t *b0, *b1, *b2, *b3;
   __device__ __forceinline__ const uint16_t *a(int i) const { return i == 0 ? a0 : a1; }
   __device__ __forceinline__ const uint16_t *b(int i) const {
@@ -194,10 +200,16 @@ __device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Pt
       // 32 rows: each wave loads 8 rows with its first 32 lanes.
       if (lane < 32) dma16(p.a(0) + koff, st + wave * 512);
     }
+    if (VAR == 0) {
 #pragma unroll
-    for (int i = 0; i < V<VAR>::B_LOADS; ++i) {
-      const uint16_t *src = PACKED ? p.b(i) + static_cast<int64_t>(kt) * B_STAGE_ELEMS : p.b(i) + koff;
-      dma16(src, st + AB + (wave * V<VAR>::B_LOADS + i) * 1024);
+      for (int i = 0; i < V<VAR>::B_LOADS; ++i)
+        dma16_buf(p.br, p.bo(i), kt * p.b_ks, st + AB + (wave * V<VAR>::B_LOADS + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V<VAR>::B_LOADS; ++i) {
+        const uint16_t *src = PACKED ? p.b(i) + static_cast<int64_t>(kt) * B_STAGE_ELEMS : p.b(i) + koff;
+        dma16(src, st + AB + (wave * V<VAR>::B_LOADS + i) * 1024);
+      }
     }
   };
   auto compute = [&](const unsigned char *st) __attribute__((always_inline)) {
@@ -495,7 +507,32 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
       const int r = wave * 8 + ((lane & 31) >> 2);
       p.set_a(0, a_row(r) + ((lane & 3) ^ ((r >> 2) & 3)) * 8);
     }
-    if (PACKED) {
+    if constexpr (VAR == 0) {
+      // The prefill second product (256 W2 rows a slab, no W3).
+      static_assert(!DUAL, "the prefill stage ring runs the second product");
+      if (PACKED) {
+        const char *Bp = static_cast<const char *>(shared ? g.Bp_shared : g.Bp_routed);
+        const int64_t slab = (shared ? 0 : static_cast<int64_t>(tl.group) * (N / SBN)) + item.y;
+        const uint32_t slab_bytes = static_cast<uint32_t>(KT * B_STAGE_ELEMS * 2);
+        p.br = buffer_rsrc(Bp + slab * slab_bytes, slab_bytes);
+        p.bo0 = static_cast<uint32_t>((wave * V<VAR>::B_LOADS + 0) * 1024 + lane * 16);
+        p.bo1 = p.bo0 + 1024;
+        p.b_ks = B_STAGE_ELEMS * 2;
+      } else {
+        const int64_t es = static_cast<int64_t>(N) * K * 2;  // one expert's matrix, bytes
+        const char *B0 = static_cast<const char *>(shared ? g.B0_shared : g.B0_routed);
+        if (!shared) B0 += tl.group * es;
+        p.br = buffer_rsrc(B0, static_cast<uint32_t>(es));
+#pragma unroll
+        for (int i = 0; i < V<VAR>::B_LOADS; ++i) {
+          const int r = (wave * V<VAR>::B_LOADS + i) * 16 + (lane >> 2);
+          const uint32_t off = static_cast<uint32_t>(static_cast<int64_t>(n0 + r) * K * 2 +
+                                                     (((lane & 3) ^ ((r >> 2) & 3)) << 4));
+          if (i == 0) p.bo0 = off; else p.bo1 = off;
+        }
+        p.b_ks = SBK * 2;
+      }
+    } else if (PACKED) {
       // The slab's stage blocks are contiguous: block kt at kt * B_STAGE_ELEMS,
       // load i of wave w at (w * B_LOADS + i) KiB in the block, lane at 16 B.
       const uint16_t *Bp = static_cast<const uint16_t *>(shared ? g.Bp_shared : g.Bp_routed);
