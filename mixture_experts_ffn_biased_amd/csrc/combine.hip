@@ -34,14 +34,14 @@ template <int KB, bool HZ, bool HR>
 __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__ O,
                                                     const uint16_t *__restrict__ Z,
                                                     const int32_t *__restrict__ inv,
-                                                    const float *__restrict__ gates, int64_t T,
+                                                    const float *__restrict__ gates,
                                                     int d, int k, const uint16_t *__restrict__ R,
                                                     uint16_t *__restrict__ y) {
   const int64_t t = blockIdx.x;
   const int nchunk = d / 8;
   __shared__ int pos[kMaxTopK];
   __shared__ float gw[kMaxTopK];
-  if (threadIdx.x < k) {
+  if (static_cast<int>(threadIdx.x) < k) {
     pos[threadIdx.x] = inv[t * k + threadIdx.x];
     gw[threadIdx.x] = gates[t * k + threadIdx.x];
   }
@@ -91,12 +91,12 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
 __global__ __launch_bounds__(256) void combine_f32(const float *__restrict__ O,
                                                    const float *__restrict__ Z,
                                                    const int32_t *__restrict__ inv,
-                                                   const float *__restrict__ gates, int64_t T, int d,
+                                                   const float *__restrict__ gates, int d,
                                                    int k, const float *__restrict__ R, float *__restrict__ y) {
   const int64_t t = blockIdx.x;
   __shared__ int pos[kMaxTopK];
   __shared__ float gw[kMaxTopK];
-  if (threadIdx.x < k) {
+  if (static_cast<int>(threadIdx.x) < k) {
     pos[threadIdx.x] = inv[t * k + threadIdx.x];
     gw[threadIdx.x] = gates[t * k + threadIdx.x];
   }
@@ -145,11 +145,11 @@ hipError_t launch_combine(const Plan &p, const float *gates, const void *residua
       default: break;
     }
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, static_cast<const uint16_t *>(p.O),
-                       static_cast<const uint16_t *>(Z), p.inv, gates, c.T, c.d, c.k,
+                       static_cast<const uint16_t *>(Z), p.inv, gates, c.d, c.k,
                        static_cast<const uint16_t *>(residual), static_cast<uint16_t *>(y));
   } else
     hipLaunchKernelGGL(combine_f32, grid, dim3(256), 0, s, static_cast<const float *>(p.O),
-                       static_cast<const float *>(Z), p.inv, gates, c.T, c.d, c.k,
+                       static_cast<const float *>(Z), p.inv, gates, c.d, c.k,
                        static_cast<const float *>(residual), static_cast<float *>(y));
   return hipGetLastError();
 }
