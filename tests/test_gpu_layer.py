@@ -129,6 +129,38 @@ DECODE = {
 }
 
 
+# The prefill streaming kernels across K: the first product's K loop (turns
+# of 12 stages) with no whole turn, a partial turn of 4 or 8 stages, or whole
+# turns only (d = 256 .. 2048), and the second product's stage ring with K
+# from 4 to 20 stages (F, F_shared from 128 to 640), with and without a
+# shared expert, softmax and grouped sigmoid routing.
+SWEEP = {
+    "sweep_d256_f640": Workload("sweep_d256_f640", 500, 256, 8, 2, 640, 0, "softmax", 1, 1, 1.0,
+                                "bf16", "uniform"),
+    "sweep_d512_f384_shared": Workload("sweep_d512_f384_shared", 700, 512, 16, 2, 384, 128, "sigmoid",
+                                       4, 2, 2.5, "bf16", "uniform"),
+    "sweep_d768_k1_shared": Workload("sweep_d768_k1_shared", 800, 768, 8, 1, 256, 256, "softmax", 1, 1,
+                                     1.0, "bf16", "uniform"),
+    "sweep_d1024_f128": Workload("sweep_d1024_f128", 600, 1024, 8, 2, 128, 0, "softmax", 1, 1, 1.0,
+                                 "bf16", "uniform"),
+    "sweep_d1536_e64_k6": Workload("sweep_d1536_e64_k6", 800, 1536, 64, 6, 256, 0, "sigmoid", 8, 4, 2.5,
+                                   "bf16", "uniform"),
+    "sweep_d2048_f512_shared": Workload("sweep_d2048_f512_shared", 520, 2048, 8, 2, 512, 384, "sigmoid",
+                                        2, 1, 2.5, "bf16", "uniform"),
+}
+
+
+@pytest.mark.parametrize("name", list(SWEEP))
+def test_stream_shapes_across_k_every_token(dev, name):
+    w = SWEEP[name]
+    assert moe.moe_plan_describe(moe.MoeConfig.from_workload(w))[0] == "stream"
+    log(f"[sweep] {name}")
+    inp = to_dev(make_inputs(w, seed=11, device="cpu"), dev)
+    y, idx, g = run(w, inp)
+    st = check_full(w, inp, y, idx, g)
+    log(f"[sweep] {name} {st}")
+
+
 @pytest.mark.parametrize("name", list(STREAM) + list(DECODE))
 def test_stream_path_every_token(dev, name):
     w = STREAM.get(name) or DECODE[name]
