@@ -16,6 +16,15 @@
 namespace moe {
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte chunk with the non-temporal hint: O, Z and R are each read once
+// here, so their lines need not displace anything in the caches.
+__device__ __forceinline__ uint4 load_once(const uint16_t *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Widens 8 bf16 values (one 16-byte chunk) into acc += g * x, or acc = x.
 __device__ __forceinline__ void fma8(float (&acc)[8], float g, const uint4 &o) {
   const uint32_t w[4] = {o.x, o.y, o.z, o.w};
@@ -50,8 +59,8 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
   for (int c = threadIdx.x; c < nchunk; c += 256) {
     const int64_t col = static_cast<int64_t>(c) * 8;
     uint4 z = {0u, 0u, 0u, 0u}, r = {0u, 0u, 0u, 0u};
-    if (HZ) z = *reinterpret_cast<const uint4 *>(Z + t * d + col);
-    if (HR) r = *reinterpret_cast<const uint4 *>(R + t * d + col);
+    if (HZ) z = load_once(Z + t * d + col);
+    if (HR) r = load_once(R + t * d + col);
     float acc[8];
     {
       const uint32_t zw[4] = {z.x, z.y, z.z, z.w};
@@ -66,7 +75,7 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
       uint4 o[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i)
-        if (KB > 0 || j0 + i < kk) o[i] = *reinterpret_cast<const uint4 *>(O + static_cast<int64_t>(pos[j0 + i]) * d + col);
+        if (KB > 0 || j0 + i < kk) o[i] = load_once(O + static_cast<int64_t>(pos[j0 + i]) * d + col);
 #pragma unroll
       for (int i = 0; i < NB; ++i)
         if (KB > 0 || j0 + i < kk) fma8(acc, gw[j0 + i], o[i]);

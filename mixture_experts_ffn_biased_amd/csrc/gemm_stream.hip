@@ -208,7 +208,10 @@ __device__ __forceinline__ void kloop(const Ring<V<VAR>::NSTAGE> &ring, const Pt
 #pragma unroll
       for (int i = 0; i < V<VAR>::B_LOADS; ++i) {
         const uint16_t *src = PACKED ? p.b(i) + static_cast<int64_t>(kt) * B_STAGE_ELEMS : p.b(i) + koff;
-        dma16(src, st + AB + (wave * V<VAR>::B_LOADS + i) * 1024);
+        // Each weight slab is read once at decode sizes: a non-temporal load
+        // keeps the stream from evicting the token rows and the router's
+        // operands (the weights of the layer exceed the last-level cache).
+        dma16<kLoadNonTemporal>(src, st + AB + (wave * V<VAR>::B_LOADS + i) * 1024);
       }
     }
   };

@@ -29,9 +29,14 @@ __device__ __forceinline__ void raw_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Cache-policy operand of a load: the non-temporal hint (gfx950's nt bit),
+// for operands that are read once (the decode variant's weight stream).
+constexpr int kLoadDefault = 0, kLoadNonTemporal = 2;
+
 // 16 bytes per lane from global memory into LDS at lds + lane * 16.
+template <int POLICY = kLoadDefault>
 __device__ __forceinline__ void dma16(const void *src, void *lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, (lds_void *)lds, 16, 0, POLICY);
 }
 
 // Raw buffer resource over bytes [base, base + bytes) (bytes < 2^32):
