@@ -35,7 +35,8 @@
 //      so each 16-row token load is one contiguous KiB.
 //  * Decode variant (few rows per expert): 32-row tiles, 4 waves each 32 x 64,
 //    an 8-slot stage ring (7 x 16 KB of weights in flight): a weight stream
-//    with a small MFMA on the side.
+//    with a small MFMA on the side.  Each slab is read once there, so its
+//    loads carry the non-temporal hint.
 //  * gate_up of the gated bodies: each wave column's 64 weight rows are 32
 //    rows of W1 then the same 32 of W3, so act(x W1^T) * (x W3^T) meets in
 //    the same lane; the bf16 result goes through LDS to 16-byte stores.  The
