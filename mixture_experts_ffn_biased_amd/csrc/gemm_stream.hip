@@ -868,11 +868,15 @@ __global__ __launch_bounds__(256) void pack_weights(const uint16_t *__restrict__
 // ---- schedule: per-XCD item lists ------------------------------------------
 
 constexpr int kMaxChunks = 4096;
+constexpr int kScheduleBlocks = 64;  // blocks of stream_schedule: 256 waves share out the chunks
 
-// One block.  Rebuilds the tile numbering of perm_scan (experts in order,
-// ceil(count/tile_m) tiles each, then the shared expert's tiles), groups tiles
-// into chunks of up to two per expert, deals chunks to XCDs round-robin and
-// writes both GEMMs' item lists (tile fastest, then n-slab, within a chunk).
+// Rebuilds the tile numbering of perm_scan (experts in order, ceil(count /
+// tile_m) tiles each, then the shared expert's tiles), groups tiles into
+// chunks of up to two per expert, deals chunks to XCDs round-robin and writes
+// both GEMMs' item lists (tile fastest, then n-slab, within a chunk).  Every
+// block derives the same chunk table from the counts; the waves of all blocks
+// then share out the chunks, a wave writing one chunk's run of items with
+// contiguous stores, and block 0 writes the list offsets and counters.
 __global__ __launch_bounds__(256) void stream_schedule(
     const int32_t *__restrict__ counts, int E, int64_t T, int has_shared, int tile_m, int nt_gu_r,
     int nt_gu_s,
@@ -943,21 +947,27 @@ __global__ __launch_bounds__(256) void stream_schedule(
     int run = 0;
     for (int x = 0; x < 8; ++x) {
       xoff[tid][x] = run;
-      meta[tid * 24 + x] = run;
-      meta[tid * 24 + 8 + x] = xtot[tid][x];
-      meta[tid * 24 + 16 + x] = 0;
+      if (blockIdx.x == 0) {
+        meta[tid * 24 + x] = run;
+        meta[tid * 24 + 8 + x] = xtot[tid][x];
+        meta[tid * 24 + 16 + x] = 0;
+      }
       run += xtot[tid][x];
     }
   }
   __syncthreads();
-  for (int ch = tid; ch < n_chunks; ch += 256) {
+  // Item q = n * mt + m of a chunk is its tile m at n-slab n (mt is 1 or 2).
+  const int lane = tid & 63;
+  const int nwaves = static_cast<int>(gridDim.x) * 4;
+  for (int ch = static_cast<int>(blockIdx.x) * 4 + (tid >> 6); ch < n_chunks; ch += nwaves) {
     const bool sh = ch >= routed_chunks;
     const int mt = cmt[ch];
+    const int first = cfirst[ch];
     for (int list = 0; list < 2; ++list) {
       const int ntl = list == 0 ? (sh ? nt_gu_s : nt_gu_r) : (sh ? nt_dn_s : nt_dn_r);
       int2 *out = (list == 0 ? items_gu : items_dn) + xoff[list][ch & 7] + cpos[list][ch];
-      for (int n = 0; n < ntl; ++n)
-        for (int m = 0; m < mt; ++m) out[n * mt + m] = make_int2(cfirst[ch] + m, n);
+      for (int q = lane; q < ntl * mt; q += 64)
+        out[q] = mt == 2 ? make_int2(first + (q & 1), q >> 1) : make_int2(first, q);
     }
   }
 }
@@ -1043,7 +1053,8 @@ hipError_t launch_pack_weights(const moe_cfg &c, int kind, const void *W1, const
 
 hipError_t launch_stream_schedule(const Plan &p, hipStream_t s) {
   const moe_cfg &c = p.cfg;
-  hipLaunchKernelGGL(stream_schedule, dim3(1), dim3(256), 0, s, p.counts, c.E, c.T, c.F_shared > 0 ? 1 : 0,
+  hipLaunchKernelGGL(stream_schedule, dim3(kScheduleBlocks), dim3(256), 0, s, p.counts, c.E, c.T,
+                     c.F_shared > 0 ? 1 : 0,
                      p.tile_m, stream_nslab_gate_up(c.F, p.kind), stream_nslab_gate_up(c.F_shared, p.kind),
                      c.d / SBN, c.d / SBN, p.items_gu,
                      p.items_dn, p.sched_meta);
