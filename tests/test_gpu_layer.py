@@ -185,6 +185,20 @@ def test_stream_path_one_expert_takes_every_token(dev):
     check_full(w, inp, y, idx, g)
 
 
+def test_decode_path_one_expert_takes_every_token(dev):
+    """Decode kernels (32-row tiles) with expert 0 in every token's set: its
+    100 rows are 4 tiles (32, 32, 32, 4) in two chunks, each tile streaming
+    the expert's weight slabs again; the shared expert has 4 tiles too."""
+    w = Workload("decode_one_expert", 100, 256, 16, 2, 256, 256, "softmax", 1, 1, 1.0, "bf16", "uniform")
+    assert moe.moe_plan_describe(moe.MoeConfig.from_workload(w))[0] == "stream_decode"
+    b = torch.zeros(w.E)
+    b[0] = 100.0
+    inp = to_dev(make_inputs(w, seed=12, device="cpu", bias=b), dev)
+    y, idx, g = run(w, inp)
+    assert (idx[:, 0] == 0).all()
+    check_full(w, inp, y, idx, g)
+
+
 PACKABLE = {
     "stream_softmax": STREAM["stream_softmax"],
     "decode_sigmoid_groups_shared": DECODE["decode_sigmoid_groups_shared"],
