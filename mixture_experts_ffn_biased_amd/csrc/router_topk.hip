@@ -481,6 +481,9 @@ __global__ __launch_bounds__(256, 2) void router_logits_split(
   raw_barrier();
   compute(ring[3]);
 
+  // The partial logits are written once and read once, so both sides carry
+  // the non-temporal hint: they need not displace u, which the gate/up
+  // gathers read again right after.
   if (wave < NB) {
     float *out = part + (static_cast<int64_t>(split) * T) * E;
 #pragma unroll
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(256, 2) void router_logits_split(
           const int row = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int col = wave * 64 + ni * 32 + (lane & 31);
           const int64_t t = t0 + row;
-          if (col < E && t < T) out[t * E + col] = acc[mi][ni][r];
+          if (col < E && t < T) __builtin_nontemporal_store(acc[mi][ni][r], &out[t * E + col]);
         }
   }
 }
@@ -521,7 +524,7 @@ __global__ __launch_bounds__(256) void router_select(const float *__restrict__ p
 #pragma unroll
     for (int sp = 0; sp < NSC; ++sp) {
       const int spc = sp < nsplit ? sp : nsplit - 1;
-      x[p][sp] = part[(static_cast<int64_t>(spc) * T + t) * E + e];
+      x[p][sp] = __builtin_nontemporal_load(&part[(static_cast<int64_t>(spc) * T + t) * E + e]);
     }
   }
 #pragma unroll
