@@ -136,6 +136,28 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return best;
 }
 
+// Maximum over each half of the wave (lanes 0-31 and 32-63), returned in
+// every lane of that half: the row maxima as in wave_max_u64, then the two
+// rows of each half.
+__device__ __forceinline__ uint64_t half_max_u64(uint64_t v) {
+  v = dpp_max_u64<0xB1>(v);
+  v = dpp_max_u64<0x4E>(v);
+  v = dpp_max_u64<0x141>(v);
+  v = dpp_max_u64<0x140>(v);
+  uint64_t row[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 16 * r));
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 16 * r));
+    row[r] = (static_cast<uint64_t>(hi) << 32) | lo;
+  }
+  const uint64_t h0 = row[0] > row[1] ? row[0] : row[1];
+  const uint64_t h1 = row[2] > row[3] ? row[2] : row[3];
+  return (threadIdx.x & 32) ? h1 : h0;
+}
+
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);

@@ -69,19 +69,36 @@ __device__ void select_token(const float *lg, const SelArgs &a, int32_t *idx_out
   if (a.G > 1) {
     // Group score: the two largest biased scores of each group.
     float my_gscore = 0.f;
-    for (int g = 0; g < a.G; ++g) {
-      uint64_t k1 = 0;
+    if (a.E == 32 * a.G && (a.E & 63) == 0) {
+      // Groups of 32: slot p of lane l is expert l + 64p, in group 2p + l/32,
+      // so each half of the wave holds one whole group per slot, and one
+      // half-wave maximum gives two groups' largest key at once.
 #pragma unroll
-      for (int p = 0; p < P; ++p)
-        if (grp[p] == g && key[p] > k1) k1 = key[p];
-      k1 = wave_max_u64(k1);
-      uint64_t k2 = 0;
+      for (int p = 0; p < P; ++p) {
+        if (2 * p >= a.G) break;
+        const uint64_t k1 = half_max_u64(key[p]);
+        const uint64_t k2 = half_max_u64(key[p] != k1 ? key[p] : 0);
+        const int sc = __float_as_int(key_value(k1) + key_value(k2));
+        const float s0 = __int_as_float(__builtin_amdgcn_readlane(sc, 0));   // group 2p
+        const float s1 = __int_as_float(__builtin_amdgcn_readlane(sc, 32));  // group 2p + 1
+        if (lane == 2 * p) my_gscore = s0;
+        if (lane == 2 * p + 1) my_gscore = s1;
+      }
+    } else {
+      for (int g = 0; g < a.G; ++g) {
+        uint64_t k1 = 0;
 #pragma unroll
-      for (int p = 0; p < P; ++p)
-        if (grp[p] == g && key[p] != k1 && key[p] > k2) k2 = key[p];
-      k2 = wave_max_u64(k2);
-      const float sc = key_value(k1) + key_value(k2);
-      if (lane == g) my_gscore = sc;
+        for (int p = 0; p < P; ++p)
+          if (grp[p] == g && key[p] > k1) k1 = key[p];
+        k1 = wave_max_u64(k1);
+        uint64_t k2 = 0;
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+          if (grp[p] == g && key[p] != k1 && key[p] > k2) k2 = key[p];
+        k2 = wave_max_u64(k2);
+        const float sc = key_value(k1) + key_value(k2);
+        if (lane == g) my_gscore = sc;
+      }
     }
     uint64_t gkey = lane < a.G ? rank_key(my_gscore, lane) : 0;
     uint64_t kept = 0;
