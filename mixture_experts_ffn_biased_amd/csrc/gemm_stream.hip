@@ -28,7 +28,8 @@
 //      two stages (64 K values, 128 B a row), so a 1 KiB load covers 8 rows
 //      x 128 B, whole cache lines of the gathered rows; 3 token slots and 4
 //      weight slots fill the 160 KiB of LDS.  Loads go through buffer
-//      resources, so the K loop adds only scalar offsets.
+//      resources, so the K loop adds only scalar offsets; weight loads carry
+//      the non-temporal hint.
 //    - Second product: the stage ring (4 slots of 32 KiB) over H, which the
 //      first product writes tile-blocked: a tile's rows K-slice by K-slice,
 //      each slice's nrows x 32 values contiguous (same size as row-major),
@@ -418,10 +419,15 @@ __device__ __forceinline__ void kloop_prefill(const PRing &ring, const PPtrs &p,
       dma16_buf(real && ((p.alive >> j) & 1) ? p.ar : none, p.ao(j), q * p.astep,
                 st + (wave * V<0>::PA_LOADS + j) * 1024);
   };
+  // A weight slab is read by at most the two tiles of its chunk, close
+  // together in time, while the gathered token rows are read again by other
+  // experts' tiles: the slab loads carry the non-temporal hint so that the
+  // weight stream does not push the token rows out of the last-level cache.
   auto issue_b = [&](unsigned char *st, int kt, bool real) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < V<0>::B_LOADS; ++i)
-      dma16_buf(real ? p.br(i) : none, p.bo(i), kt * p.bstep, st + (wave * V<0>::B_LOADS + i) * 1024);
+      dma16_buf<kLoadNonTemporal>(real ? p.br(i) : none, p.bo(i), kt * p.bstep,
+                                  st + (wave * V<0>::B_LOADS + i) * 1024);
   };
   // half: which 32 of the token slot's 64 K values this stage multiplies.
   auto compute = [&](const unsigned char *sta, int half, const unsigned char *stb) __attribute__((always_inline)) {

@@ -30,7 +30,8 @@ __device__ __forceinline__ void raw_barrier() {
 }
 
 // Cache-policy operand of a load: the non-temporal hint (gfx950's nt bit),
-// for operands that are read once (the decode variant's weight stream).
+// for operand streams that should not displace data read again later (the
+// weight streams of the decode kernels and of the prefill gate/up kernel).
 constexpr int kLoadDefault = 0, kLoadNonTemporal = 2;
 
 // 16 bytes per lane from global memory into LDS at lds + lane * 16.
@@ -49,8 +50,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
 
 // The same 16-byte load into LDS through a buffer resource: the base and the
 // scalar offset stay in SGPRs, only the 32-bit lane offset is a VGPR.
+template <int POLICY = kLoadDefault>
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, void *lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, static_cast<int>(voff), soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, static_cast<int>(voff), soff, 0, POLICY);
 }
 
 }  // namespace moe
