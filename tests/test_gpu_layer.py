@@ -382,6 +382,22 @@ def test_dsv3_decode_full_size(dev):
     del inp
 
 
+@pytest.mark.parametrize("name,seed", [("dsv3_prefill", 1), ("dsv3_decode", 2)])
+def test_dsv3_full_size_other_seed_plain_and_packed(dev, name, seed):
+    """Another draw of every input at full size: routing of all tokens and
+    sampled outputs against the oracle, and the packed-weight layer bitwise
+    equal to the plain one."""
+    w = WORKLOADS[name]
+    inp = make_inputs(w, seed=seed, device=dev)
+    y, idx, g, _ = check_large(w, inp, n_sample=8, seed=seed)
+    cfg = moe.MoeConfig.from_workload(w)
+    packed = moe.moe_pack_weights(inp["W1"], inp["W3"], inp["W2"], inp["shared"], cfg=cfg)
+    yp, ip, gp = moe.moe_layer_forward_packed(inp["u"], inp["W_router"], inp["bias"], packed, cfg=cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(ip, idx) and torch.equal(gp, g) and torch.equal(yp, y)
+    del inp, packed
+
+
 def test_streaming_schedule_overflow_falls_back_to_the_tiled_kernels(dev):
     """720,000 tokens: more expert chunks than the streaming schedule holds, so
     the layer runs on the tiled kernels (11,258 tiles); routing of every token
