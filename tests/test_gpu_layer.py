@@ -126,6 +126,11 @@ DECODE = {
                                              "sigmoid", 4, 2, 2.5, "bf16", "uniform"),
     "decode_softmax_e64": Workload("decode_softmax_e64", 37, 512, 64, 6, 512, 0, "softmax", 1, 1,
                                    1.0, "bf16", "uniform"),
+    # one token: every tile (four routed, the shared expert's) holds a single row
+    "decode_one_token": Workload("decode_one_token", 1, 256, 16, 4, 256, 256, "sigmoid", 4, 2, 2.5,
+                                 "bf16", "uniform"),
+    "decode_two_tokens_k8": Workload("decode_two_tokens_k8", 2, 512, 64, 8, 256, 256, "softmax", 1, 1,
+                                     1.0, "bf16", "uniform"),
 }
 
 
