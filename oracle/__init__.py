@@ -11,8 +11,10 @@ Three parts, all fp64:
   stable top-k, gates from raw scores, experts (SwiGLU, GEGLU, or the GELU
   MLP with biases), unweighted shared expert, gate-weighted sum -- plus the
   expert-contiguous permutation.
-* ``expert_major.py``: an independent second implementation that follows the
-  expert-major masked loop of "Mixture of experts and architecture families",
+* ``expert_major.py``: an independent second implementation, expert-major in
+  the dispatch / combine form (flattened (token, slot) pairs grouped by
+  expert, one batched product per expert, scatter-add of the weighted rows),
+  with the softmax router of "Mixture of experts and architecture families",
   "The router and load balancing" (NumPy float64).
 * ``balance.py``: the auxiliary-loss-free bias loop and the routing entropy of
   "Mixture of Experts and Hybrid Architectures", "Aux-loss-free balance loop".

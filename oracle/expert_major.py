@@ -10,9 +10,13 @@ raw-logit route of "Mixture of Experts and Hybrid Architectures", "The router in
 code" (softmax is monotone) and a renormalised subset of a softmax equals a
 softmax over that subset, so the two oracles must agree.
 
-The expert loop is the same page's masked loop: for each expert, take the rows
-whose selection contains it, run the expert on those rows, weight and add.
-Experts are SwiGLU ("Sparse MoE FFN" (DeepSeek-V3), "How it works"):
+The expert pass is expert-major, in the dispatch / combine form the "Sparse
+MoE FFN" page describes in "Packed forward" (gather each expert's tokens, run
+it once on them, scatter-add the weighted result): the T*k (token, slot) pairs
+are flattened, grouped by expert, each expert runs once on its gathered rows
+as a batched matrix product, and the gate-weighted rows are scattered back
+into the output with an unbuffered add.  Experts are SwiGLU ("Sparse MoE FFN"
+(DeepSeek-V3), "How it works"):
 W2 (SiLU(W1 x) * W3 x); or GEGLU, GELU in place of SiLU (named beside SwiGLU
 in the cheat sheet's "Calculator defaults"); or the biased GELU
 MLP of "Lesson 2 -- From the Dense FFN to a Layer of Experts", section 2:
@@ -72,21 +76,29 @@ def layer(u, W_router, W1, W3, W2, k, shared=None, idx=None, gates=None, kind=SW
           b1=None, b2=None):
     """Expert-major layer output.  With idx/gates None the softmax router above
     chooses; otherwise the given selection and gates are used (so the expert
-    loop can also be checked under sigmoid, group-limited routing).
+    pass can also be checked under sigmoid, group-limited routing).
     shared is (W1s, W3s, W2s[, b1s, b2s]); W3 is None for the GELU MLP."""
-    u = widen(u)
+    x = widen(u)
     W1, W3, W2, b1, b2 = (_w(a) for a in (W1, W3, W2, b1, b2))
     if idx is None:
-        idx, gates = softmax_router(u, widen(W_router), k)
-    out = np.zeros_like(u)
-    for e in range(W1.shape[0]):
-        mask = idx == e
-        rows = mask.any(axis=1)
-        if rows.any():
-            w = (gates * mask)[rows].sum(axis=1, keepdims=True)
-            out[rows] += w * expert(u[rows], kind, W1[e], None if W3 is None else W3[e], W2[e],
-                                    None if b1 is None else b1[e], None if b2 is None else b2[e])
+        idx, gates = softmax_router(x, widen(W_router), k)
+    idx = np.asarray(idx, dtype=np.int64)
+    gates = np.asarray(gates, dtype=np.float64)
+    n_tok, n_slot = idx.shape
+    # dispatch: one entry per (token, slot) pair, flattened
+    tok_of = np.repeat(np.arange(n_tok), n_slot)
+    exp_of = idx.reshape(-1)
+    wgt_of = gates.reshape(-1)
+    y = np.zeros((n_tok, x.shape[1]))
+    for e in np.unique(exp_of):
+        (pairs,) = np.nonzero(exp_of == e)
+        toks = tok_of[pairs]
+        ye = expert(x[toks], kind, W1[e], None if W3 is None else W3[e], W2[e],
+                    None if b1 is None else b1[e], None if b2 is None else b2[e])
+        # combine: scatter-add each pair's weighted row into its token
+        np.add.at(y, toks, wgt_of[pairs, None] * ye)
     if shared is not None:
-        sh = [_w(a) for a in shared] + [None] * (5 - len(shared))
-        out += expert(u, kind, *sh)
-    return out, idx, gates
+        sw = [_w(a) for a in shared]
+        sw += [None] * (5 - len(sw))
+        y += expert(x, kind, *sw)
+    return y, idx.astype(np.int32), gates
