@@ -39,15 +39,39 @@ def test_roofline_takes_the_longer_lower_bound():
                                                      abs=0.05)
 
 
-def test_gate_up_bytes_at_the_deepseek_v3_prefill_shape():
+def test_gate_up_work_at_the_deepseek_v3_prefill_shape():
     # Every one of the 256 experts hit: W1 and W3 of each (2 * 2048 * 7168 bf16) and of the shared
-    # expert, each of the 65,536 slots' token rows and the 8192 shared rows read once, and their
-    # 2048-wide activations written once.
+    # expert, the token matrix u read once (8192 x 7168), and the 2048-wide activations of the
+    # 65,536 routed slots and of the 8192 shared rows written once: 15.51 GB for 4.329 TFLOP.
     w = WORKLOADS["dsv3_prefill"]
     weights = (256 * 2 * 2048 * 7168 + 2 * 2048 * 7168) * 2
-    rows = (8192 * 8 + 8192) * 7168 * 2
+    u_once = 8192 * 7168 * 2
     acts = (8192 * 8 * 2048 + 8192 * 2048) * 2
-    assert bench.gate_up_bytes(w, 256) == weights + rows + acts == 16_450_060_288
+    assert bench.gate_up_bytes(w, 256) == weights + u_once + acts == 15_510_536_192
+    assert bench.gate_up_flops(w) == 4 * 7168 * (2048 * 8192 * 8 + 2048 * 8192) == 4_329_327_034_368
+
+
+def test_layer_work_at_the_deepseek_v3_prefill_shape():
+    # T (2 d E + 6 d F k + 6 d F_s) = 6.524 TFLOP; router matrix + bias, 257 experts' three
+    # matrices, u and y, indices and gates = 22.88 GB (all 256 experts hit).
+    w = WORKLOADS["dsv3_prefill"]
+    assert w.flops == 8192 * (2 * 7168 * 256 + 6 * 7168 * 2048 * 8 + 6 * 7168 * 2048) == 6_524_055_322_624
+    nbytes = (256 * 7168 * 2 + 4 * 256 + 256 * 3 * 7168 * 2048 * 2 + 3 * 7168 * 2048 * 2
+              + 2 * 8192 * 7168 * 2 + 8 * 8192 * 8)
+    assert bench.layer_bytes(w, 256) == nbytes == 22_875_735_040
+
+
+def test_prefill_roofline_is_taken_against_the_mfma_peak():
+    # The C3 gate/up kernel at 4.4283 ms: 977.6 TFLOP/s = 0.391 of the MFMA peak, although its
+    # 279 FLOP/B lie under the 312.5 FLOP/B ridge; the HBM fraction is reported beside it.
+    w = WORKLOADS["dsv3_prefill"]
+    r = bench.roofline("gate_up", bench.gate_up_flops(w), bench.gate_up_bytes(w, 256), 4.4283,
+                       19_222_097_902, bound="mfma")
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert r["frac"] == pytest.approx(0.3911, abs=1e-4)
+    assert r["flop_per_byte"] == pytest.approx(279.1, abs=0.1)
+    assert r["hbm_frac"] == pytest.approx(15_510_536_192 / 4.4283e-3 / 8e12, abs=1e-4)
+    assert r["traffic_over_alg"] == pytest.approx(1.239, abs=1e-3)
 
 
 def test_stored_traffic_is_used_only_for_the_current_kernel_source(tmp_path, monkeypatch):
