@@ -186,7 +186,7 @@ def run_layer(w, inp, u, steps, warmup, torch, packed=None):
                                   workspace=ws)
 
     ms, wall, stage_ms, calls = timed_steps(step, steps, warmup, torch)
-    return ms, wall, stage_ms, idx
+    return ms, wall, stage_ms, idx, (y, gates)
 
 
 def graph_ms(w, inp, u, packed, steps, torch):
@@ -246,7 +246,7 @@ def time_shape(w, inp, steps, warmup, torch, bias=None):
     packed = moe.moe_pack_weights(inp["W1"], inp["W3"], inp["W2"], inp["shared"], cfg=cfg)
     if bias is not None:
         inp = dict(inp, bias=bias)
-    ms, _, stage_ms, idx = run_layer(w, inp, inp["u"], steps, warmup, torch, packed)
+    ms, _, stage_ms, idx, _ = run_layer(w, inp, inp["u"], steps, warmup, torch, packed)
     hit = int(torch.unique(idx).numel())
     del packed
     return layer_record(w, ms, stage_ms, hit, moe.moe_plan_describe(cfg)[0]), idx
@@ -352,48 +352,127 @@ def other_configs(args, torch, dev):
     return out
 
 
-def cpu_baseline(w, inp, n_tokens, seed):
+def tile_edge_tokens(w, inp, u, torch):
+    """Tokens in the first and last row of every routed and shared tile the
+    grouped GEMMs run for this input (from the library's own permutation):
+    where an error in a tile's row range would show."""
+    import numpy as np
+
+    import mixture_experts_ffn_biased_amd as moe
+    cfg = moe.MoeConfig.from_workload(w)
+    path, tile_m = moe.moe_plan_describe(cfg)
+    _, _, counts, offsets, perm, _ = moe.moe_route_debug(u, inp["W_router"], inp["bias"], cfg=cfg)
+    counts, offsets, perm = counts.cpu().numpy(), offsets.cpu().numpy(), perm.cpu().numpy()
+    toks = set()
+
+    def edges(base, c, is_shared):
+        nt = -(-c // tile_m)
+        for i in range(nt):
+            if path == "stream":  # rows spread evenly over the expert's tiles
+                q, r = divmod(c, nt)
+                r0, n = i * q + min(i, r), q + (1 if i < r else 0)
+            else:
+                r0, n = i * tile_m, min(tile_m, c - i * tile_m)
+            for row in (r0, r0 + n - 1):
+                toks.add(int(row) if is_shared else int(perm[base + row]) // w.k)
+    for e in range(w.E):
+        edges(int(offsets[e]), int(counts[e]), False)
+    if w.Fs:
+        edges(0, w.T, True)
+    return np.array(sorted(toks), dtype=np.int64)
+
+
+def oracle_check(w, u_host, Wr, bias, W, used, gpu_y, gpu_idx, gpu_gates, tok, threads):
+    """The oracle's routing of every token and its outputs for the tokens
+    `tok`, compared with the GPU's: near-tie counts (k-th / (k+1)-th biased
+    expert score or M-th / (M+1)-th group score within 1e-5 relative), tokens
+    whose expert set differs without a near-tie, the largest gate error and
+    the largest per-token relative L2 error of y.  A near-tie token the GPU
+    broke the other way is compared with the oracle run on the GPU's choice."""
+    import numpy as np
+
+    import oracle
+    mode = oracle.SIGMOID if w.score_fn == "sigmoid" else oracle.SOFTMAX
+    t = time.perf_counter()
+    ir, gr, ge, gg, _ = oracle.route(u_host, Wr, w.k, mode, w.n_groups, w.topk_groups, w.route_scale,
+                                     bias=bias, nthreads=threads)
+    t_route = time.perf_counter() - t
+    near = (ge < 1e-5) | (gg < 1e-5)
+    same = (np.sort(gpu_idx, 1) == np.sort(ir, 1)).all(1)
+    ok = same & ~near
+    g = np.take_along_axis(gpu_gates.astype(np.float64)[ok], np.argsort(gpu_idx[ok], 1), 1)
+    r = np.take_along_axis(gr[ok], np.argsort(ir[ok], 1), 1)
+    gate_err = float((np.abs(g - r) / np.maximum(1.0, np.abs(r))).max()) if g.size else 0.0
+    sel = np.where(near[tok, None], gpu_idx[tok], ir[tok]).astype(np.int64)
+    remap = np.full(w.E, -1, dtype=np.int64)
+    remap[used] = np.arange(used.size)
+    assert (remap[sel] >= 0).all()
+    W1, W3, W2, shared = W
+    t = time.perf_counter()
+    yr, _, _, _, _ = oracle.forward(u_host[tok], Wr[used], W1, W3, W2, w.k, shared=shared, score_fn=mode,
+                                    route_scale=w.route_scale, forced_idx=remap[sel], nthreads=threads)
+    t_ffn = time.perf_counter() - t
+    yg = oracle.widen(gpu_y[tok])
+    err = np.linalg.norm(yg - yr, axis=1) / np.maximum(np.linalg.norm(yr, axis=1), 1e-30)
+    tol = 1e-2 if w.dtype == "bf16" else 1e-5
+    rec = {"tokens_routed": int(w.T), "near_ties": int(near.sum()),
+           "near_tie_diffs": int((~same & near).sum()),
+           "set_mismatches_without_near_tie": int((~same & ~near).sum()),
+           "gate_err_max": gate_err, "outputs_checked": int(tok.size),
+           "rel_l2_max": float(err.max()), "rel_l2_tol": tol}
+    rec["pass"] = rec["set_mismatches_without_near_tie"] == 0 and gate_err <= 1e-5 and rec["rel_l2_max"] <= tol
+    return rec, t_route, t_ffn
+
+
+def cpu_baseline(w, inp, n_tokens, seed, gpu_out, edge_tok, decode=None):
     """The oracle, as it stands, on the host cores: routing of every token and
-    the expert outputs of n_tokens sampled tokens."""
+    the expert outputs of a bounded sample of tokens -- the tokens in the
+    first and last row of every GEMM tile, then seeded random ones up to
+    n_tokens.  The same oracle results give the parity record of the timed
+    run's outputs (gpu_out: y, topk_idx, gates), and of the decode-shaped
+    layer's (decode: workload, u, y, topk_idx, gates; every token)."""
     import numpy as np
     import torch
 
     import oracle
     from synthetic import to_numpy
 
-    mode = oracle.SIGMOID if w.score_fn == "sigmoid" else oracle.SOFTMAX
     u = to_numpy(inp["u"])
     Wr = to_numpy(inp["W_router"])
     bias = inp["bias"].double().cpu().numpy()
     threads = oracle.default_threads()
-    t = time.perf_counter()
-    idx, _, _, _, _ = oracle.route(u, Wr, w.k, mode, w.n_groups, w.topk_groups, w.route_scale,
-                                   bias=bias, nthreads=threads)
-    t_route = time.perf_counter() - t
     rng = np.random.default_rng(seed)
-    tok = np.sort(rng.choice(w.T, size=min(n_tokens, w.T), replace=False))
-    sel = idx[tok].astype(np.int64)
-    used = np.unique(sel)
-    remap = np.full(w.E, -1, dtype=np.int64)
-    remap[used] = np.arange(used.size)
+    rest = np.setdiff1d(np.arange(w.T), edge_tok)
+    extra = max(0, min(n_tokens, w.T) - edge_tok.size)
+    tok = np.sort(np.concatenate([edge_tok, rng.choice(rest, size=min(extra, rest.size), replace=False)]))
+    gi = gpu_out[1].cpu().numpy().astype(np.int64)
+    # every expert either layer's checked tokens may use: the GPU's and the oracle's choice
+    used = np.arange(w.E)
     t = time.perf_counter()
-    ui = torch.from_numpy(used).to(inp["W1"].device)
-    W1 = to_numpy(inp["W1"].index_select(0, ui))
-    W3 = to_numpy(inp["W3"].index_select(0, ui))
-    W2 = to_numpy(inp["W2"].index_select(0, ui))
+    W1 = to_numpy(inp["W1"])
+    W3 = to_numpy(inp["W3"])
+    W2 = to_numpy(inp["W2"])
     shared = None if inp["shared"] is None else tuple(to_numpy(x) for x in inp["shared"])
     t_copy = time.perf_counter() - t
-    t = time.perf_counter()
-    oracle.forward(u[tok], Wr[used], W1, W3, W2, w.k, shared=shared, score_fn=mode,
-                   route_scale=w.route_scale, forced_idx=remap[sel], nthreads=threads)
-    t_ffn = time.perf_counter() - t
+    W = (W1, W3, W2, shared)
+    par, t_route, t_ffn = oracle_check(w, u, Wr, bias, W, used, to_numpy(gpu_out[0]), gi,
+                                       gpu_out[2].cpu().numpy(), tok, threads)
+    par["tile_edge_tokens"] = int(edge_tok.size)
+    parity = {w.name: par}
     n = tok.size
     value = n / (t_ffn + t_route * n / w.T)
-    return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    if decode is not None:
+        wd, ud, yd, idd, gd = decode
+        pd, _, _ = oracle_check(wd, to_numpy(ud), Wr, bias, W, used, to_numpy(yd),
+                                idd.cpu().numpy().astype(np.int64), gd.cpu().numpy(), np.arange(wd.T), threads)
+        parity[wd.name] = pd
+    base = {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"{w.name}: routing of all {w.T} tokens ({t_route:.2f} s) + expert and "
-                       f"shared outputs of {n} seeded random tokens ({t_ffn:.2f} s); tokens/s = "
-                       f"n / (t_ffn + t_route * n / T); device-to-host copy of the "
-                       f"{used.size} experts used ({t_copy:.2f} s) excluded")}
+                       f"shared outputs of {n} tokens: the {edge_tok.size} in the first or last row of a "
+                       f"GEMM tile and seeded random ones ({t_ffn:.2f} s); tokens/s = "
+                       f"n / (t_ffn + t_route * n / T); device-to-host copy of the weights "
+                       f"({t_copy:.2f} s) excluded")}
+    return base, parity
 
 
 def main():
@@ -423,7 +502,8 @@ def main():
         packed = moe.moe_pack_weights(inp["W1"], inp["W3"], inp["W2"], inp["shared"], cfg=cfg)
         torch.cuda.synchronize()
     log(f"[bench] {w.name}: {args.warmup} warm-up + {args.steps} timed steps")
-    ms, wall, stage_ms, idx = run_layer(w, inp, inp["u"], args.steps, args.warmup, torch, packed)
+    ms, wall, stage_ms, idx, (y_out, g_out) = run_layer(w, inp, inp["u"], args.steps, args.warmup, torch,
+                                                        packed)
     tokens_per_s = w.T / (ms * 1e-3)
     layer_tflops = w.flops / (ms * 1e-3) / 1e12
     hit_p = int(torch.unique(idx).numel())
@@ -500,7 +580,8 @@ def main():
         wd = WORKLOADS[args.decode_workload]
         ud = make_u(wd, seed=args.seed, device=dev)
         log(f"[bench] {wd.name}: {args.warmup} warm-up + {args.decode_steps} timed steps")
-        dms, _, dstage, didx = run_layer(wd, inp, ud, args.decode_steps, args.warmup, torch, packed)
+        dms, _, dstage, didx, (yd_out, gd_out) = run_layer(wd, inp, ud, args.decode_steps, args.warmup, torch,
+                                                           packed)
         hit = int(torch.unique(didx).numel())
         dbytes = layer_bytes(wd, hit)
         gbs = dbytes / (dms * 1e-3) / 1e9
@@ -522,7 +603,7 @@ def main():
 
     if packed is not None and not args.no_plain:
         # the same layer with the weights in their plain layout, for reference
-        pms, _, pstage, _ = run_layer(w, inp, inp["u"], max(3, args.steps // 2), 2, torch, None)
+        pms, _, pstage, _, _ = run_layer(w, inp, inp["u"], max(3, args.steps // 2), 2, torch, None)
         result["plain_weights"] = {"ms_per_step": round(pms, 4),
                                    "tokens_per_s": round(w.T / (pms * 1e-3), 1),
                                    "stage_ms": {n: round(v, 4) for n, v in zip(moe.STAGES, pstage)}}
@@ -543,8 +624,11 @@ def main():
         del src, dst
 
     if not args.no_cpu_baseline:
-        log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
-        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens, args.seed)
+        log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens, parity of the timed outputs")
+        edge = tile_edge_tokens(w, inp, inp["u"], torch)
+        dec = None if args.no_decode else (wd, ud, yd_out, didx, gd_out)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(
+            w, inp, args.cpu_tokens, args.seed, (y_out, idx, g_out), edge, decode=dec)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -8,7 +8,9 @@ raises instead of computing anything another way.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 from typing import Optional, Sequence
@@ -220,6 +222,19 @@ def _stream(device, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(fn):
+    """Runs an entry-point wrapper with the caller's `stream` current, so that
+    the outputs and the workspace it allocates belong to the stream the
+    kernels run on (torch's caching allocator then never hands their memory
+    to other work while those kernels may still use it)."""
+    @functools.wraps(fn)
+    def wrapped(*args, stream=None, **kw):
+        ctx = contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+        with ctx:
+            return fn(*args, stream=stream, **kw)
+    return wrapped
+
+
 def alloc_workspace(cfg: MoeConfig, device) -> torch.Tensor:
     n = moe_workspace_bytes(cfg)
     if n == 0 and cfg.T > 0:
@@ -227,6 +242,7 @@ def alloc_workspace(cfg: MoeConfig, device) -> torch.Tensor:
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
+@_on_stream
 def moe_layer_forward(u, W_router, bias, W1, W3, W2, shared: Optional[Sequence] = None, *,
                       cfg: MoeConfig, y=None, topk_idx=None, gates=None, workspace=None,
                       stream=None):
@@ -337,6 +353,7 @@ def _workspace_ex(cfg, kind, dev, workspace):
     return workspace
 
 
+@_on_stream
 def moe_layer_forward_ex(u, W_router, bias, kind, W1, W3, W2, b1=None, b2=None, shared=None, *,
                          cfg: MoeConfig, y=None, topk_idx=None, gates=None, workspace=None, stream=None):
     """moe_layer_forward with experts of the given kind ("swiglu", "geglu", "gelu_mlp").
@@ -365,6 +382,7 @@ def moe_packed_weights_bytes_ex(cfg: MoeConfig, kind) -> int:
     return int(lib().moe_packed_weights_bytes_ex(ctypes.byref(c), _kind(kind)))
 
 
+@_on_stream
 def moe_pack_weights_ex(kind, W1, W3, W2, shared=None, *, cfg: MoeConfig, packed=None, stream=None):
     """One-time re-layout of the weights of experts of the given kind; returns
     the packed uint8 buffer (biases are not packed).  shared: None or
@@ -384,6 +402,7 @@ def moe_pack_weights_ex(kind, W1, W3, W2, shared=None, *, cfg: MoeConfig, packed
     return packed
 
 
+@_on_stream
 def moe_layer_forward_packed_ex(u, W_router, bias, kind, packed, b1=None, b2=None, b1s=None, b2s=None, *,
                                 cfg: MoeConfig, y=None, topk_idx=None, gates=None, workspace=None,
                                 stream=None):
@@ -411,6 +430,7 @@ def moe_packed_weights_bytes(cfg: MoeConfig) -> int:
     return int(lib().moe_packed_weights_bytes(ctypes.byref(c)))
 
 
+@_on_stream
 def moe_pack_weights(W1, W3, W2, shared: Optional[Sequence] = None, *, cfg: MoeConfig,
                      packed=None, stream=None):
     """One-time re-layout of the expert weights; returns the packed uint8 buffer."""
@@ -441,6 +461,7 @@ def moe_pack_weights(W1, W3, W2, shared: Optional[Sequence] = None, *, cfg: MoeC
     return packed
 
 
+@_on_stream
 def moe_layer_forward_packed(u, W_router, bias, packed, *, cfg: MoeConfig, y=None, topk_idx=None,
                              gates=None, workspace=None, stream=None):
     """moe_layer_forward with weights from moe_pack_weights."""
@@ -472,6 +493,7 @@ def moe_layer_forward_packed(u, W_router, bias, packed, *, cfg: MoeConfig, y=Non
     return y, topk_idx, gates
 
 
+@_on_stream
 def moe_rmsnorm(h, norm_weight, eps: float, *, out=None, stream=None):
     """out = h / sqrt(mean(h^2, -1) + eps) * norm_weight, rows of h [T][d] (bf16 or fp32)."""
     dev = h.device
@@ -517,6 +539,7 @@ def _block_outputs(cfg, dev, y, topk_idx, gates):
     return y, topk_idx, gates
 
 
+@_on_stream
 def moe_block_forward(h, norm_weight, norm_eps, W_router, bias, W1, W3, W2, shared=None, *, cfg: MoeConfig,
                       y=None, topk_idx=None, gates=None, workspace=None, stream=None):
     """y = h + MoE(RMSNorm(h)); returns (y, topk_idx, gates)."""
@@ -551,6 +574,7 @@ def moe_block_forward(h, norm_weight, norm_eps, W_router, bias, W1, W3, W2, shar
     return y, topk_idx, gates
 
 
+@_on_stream
 def moe_block_forward_packed(h, norm_weight, norm_eps, W_router, bias, packed, *, cfg: MoeConfig, y=None,
                              topk_idx=None, gates=None, workspace=None, stream=None):
     """moe_block_forward with weights from moe_pack_weights."""
@@ -575,6 +599,7 @@ def moe_block_forward_packed(h, norm_weight, norm_eps, W_router, bias, packed, *
     return y, topk_idx, gates
 
 
+@_on_stream
 def moe_route_debug(u, W_router, bias, *, cfg: MoeConfig, workspace=None, stream=None):
     """Routing + permutation only: (topk_idx, gates, counts, offsets, perm, inv)."""
     dev = u.device
@@ -603,6 +628,7 @@ def moe_route_debug(u, W_router, bias, *, cfg: MoeConfig, workspace=None, stream
     return topk_idx, gates, counts, offsets, perm, inv
 
 
+@_on_stream
 def moe_balance_update(topk_idx, bias, *, E: int, gamma: float = 0.15, counts=None, entropy=None,
                        stream=None):
     """One aux-loss-free balance step on the routing topk_idx [T][k] (int32):

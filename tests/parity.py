@@ -23,6 +23,15 @@ TIE_TOL = 1e-5
 GATE_TOL = 1e-5
 Y_TOL = {"bf16": 1e-2, "f32": 1e-5}
 
+# Per-case parity statistics of this test session (near-tie counts, the
+# largest rel-L2, tokens and tiles checked); conftest writes them to the
+# JSON file named by MOE_PARITY_RECORD at the end of the session.
+RECORD = {}
+
+
+def record(name, stats):
+    RECORD[name] = dict(stats)
+
 
 def mode_of(w):
     return oracle.SIGMOID if w.score_fn == "sigmoid" else oracle.SOFTMAX
@@ -109,3 +118,49 @@ def sampled_outputs(w, inp, tokens, sel, nthreads=None):
         u, Wr, W1, W3, W2, w.k, shared=shared, score_fn=mode_of(w), n_groups=1, topk_groups=1,
         route_scale=w.route_scale, forced_idx=remap[sel], nthreads=nthreads)
     return y, used[idx], gates
+
+
+def tile_spans(path, tile_m, counts, n_tokens, has_shared):
+    """Row spans (expert, first position, rows) of every tile the grouped GEMMs
+    run: each expert's rows in tiles of at most tile_m, spread evenly over
+    ceil(c / tile_m) tiles on the prefill streaming path and in full tiles with
+    a ragged last one elsewhere, then the shared expert's T rows the same way.
+    Positions index the expert-contiguous order (offsets[e] + row)."""
+    balanced = path == "stream"
+    spans = []
+
+    def split(e, base, c):
+        nt = -(-c // tile_m)
+        for i in range(nt):
+            if balanced:
+                q, r = divmod(c, nt)
+                r0, n = i * q + min(i, r), q + (1 if i < r else 0)
+            else:
+                r0, n = i * tile_m, min(tile_m, c - i * tile_m)
+            spans.append((e, base + r0, n))
+
+    off = 0
+    for e, c in enumerate(np.asarray(counts).tolist()):
+        split(e, off, int(c))
+        off += int(c)
+    if has_shared:
+        split(len(counts), 0, int(n_tokens))
+    return spans
+
+
+def tile_edge_tokens(w, path, tile_m, counts, perm, n_tokens):
+    """Tokens that sit in the first and last row of every routed and shared
+    tile, and in the rows either side of the 128-row split of a 256-row tile
+    (the two wave rows of the prefill kernels): the rows where a wrong tile
+    offset, row count or row-group bound would show."""
+    perm = np.asarray(perm, dtype=np.int64)
+    E = len(counts)
+    toks = set()
+    spans = tile_spans(path, tile_m, counts, n_tokens, w.Fs > 0)
+    for e, p0, n in spans:
+        rows = {0, n - 1}
+        if n > 128:
+            rows |= {127, 128}
+        for r in rows:
+            toks.add(int(p0 + r) if e == E else int(perm[p0 + r] // w.k))
+    return np.array(sorted(toks), dtype=np.int64), len(spans)

@@ -88,3 +88,43 @@ def test_stored_traffic_is_used_only_for_the_current_kernel_source(tmp_path, mon
     assert bench.stored_traffic("fresh") == 42
     assert bench.stored_traffic("stale") is None
     assert bench.stored_traffic("missing") is None
+
+
+def test_parity_record_of_the_cpu_leg_on_oracle_outputs():
+    # The bench's parity report, fed the oracle's own routing and outputs (rounded to bf16) as the
+    # "GPU" result: it must pass; a planted wrong expert on a token that is not a near-tie, and a
+    # planted output error of 2 % on one token, must each fail it.
+    import numpy as np
+    import torch
+
+    import oracle
+    from synthetic import make_inputs, to_numpy
+    w = WORKLOADS["dsv3_prefill"].with_(name="small_dsv3", T=96, d=128, E=32, F=64, Fs=64)
+    inp = make_inputs(w, seed=3, device="cpu")
+    u, Wr = to_numpy(inp["u"]), to_numpy(inp["W_router"])
+    W1, W3, W2 = (to_numpy(inp[n]) for n in ("W1", "W3", "W2"))
+    shared = tuple(to_numpy(t) for t in inp["shared"])
+    bias = inp["bias"].double().numpy()
+    y, idx, g, ge, gg = oracle.forward(u, Wr, W1, W3, W2, w.k, bias=bias, shared=shared,
+                                       score_fn=oracle.SIGMOID, n_groups=w.n_groups,
+                                       topk_groups=w.topk_groups, route_scale=w.route_scale)
+    ybf = torch.from_numpy(y).to(torch.bfloat16)
+    yg = to_numpy(ybf)
+    tok = np.arange(0, w.T, 3)
+    args = (w, u, Wr, bias, (W1, W3, W2, shared), np.arange(w.E))
+    rec, _, _ = bench.oracle_check(*args, yg, idx.astype(np.int64), g.astype(np.float32), tok, 2)
+    assert rec["pass"] and rec["outputs_checked"] == tok.size and rec["tokens_routed"] == w.T
+    assert rec["near_ties"] == int(((ge < 1e-5) | (gg < 1e-5)).sum())
+    assert rec["rel_l2_max"] < 4e-3
+    # a wrong expert on a token that is not a near-tie
+    t = int(np.nonzero((ge >= 1e-5) & (gg >= 1e-5))[0][0])
+    bad = idx.astype(np.int64).copy()
+    bad[t, -1] = next(e for e in range(w.E) if e not in bad[t])
+    rec, _, _ = bench.oracle_check(*args, yg, bad, g.astype(np.float32), tok, 2)
+    assert not rec["pass"] and rec["set_mismatches_without_near_tie"] == 1
+    # a 2 % error on one checked token's output
+    y2 = y.copy()
+    y2[tok[1]] *= 1.02
+    rec, _, _ = bench.oracle_check(*args, to_numpy(torch.from_numpy(y2).to(torch.bfloat16)),
+                                   idx.astype(np.int64), g.astype(np.float32), tok, 2)
+    assert not rec["pass"] and rec["rel_l2_max"] > 1e-2

@@ -15,8 +15,8 @@ import torch
 import mixture_experts_ffn_biased_amd as moe
 import oracle
 from oracle import balance, skew
-from parity import (Y_TOL, host, mode_of, oracle_inputs, rel_l2, route_parity, sampled_outputs,
-                    widen_gpu)
+from parity import (Y_TOL, host, mode_of, oracle_inputs, record, rel_l2, route_parity, sampled_outputs,
+                    tile_edge_tokens, widen_gpu)
 from synthetic import WORKLOADS, Workload, make_inputs, make_u
 
 pytestmark = pytest.mark.gpu
@@ -82,6 +82,8 @@ def check_full(w, inp, y, idx, g):
     err = rel_l2(widen_gpu(y), yr)
     assert err.max() <= Y_TOL[w.dtype], f"max rel-L2 {err.max():.3e} at token {err.argmax()}"
     st["rel_l2_max"] = float(err.max())
+    st["outputs_checked"] = int(w.T)
+    record(w.name, st)
     return st
 
 
@@ -283,6 +285,30 @@ def test_nan_row_gives_valid_distinct_indices(dev):
     assert gi[7].tolist() == ir[7].tolist()
 
 
+def test_side_stream_call_matches_the_default_stream(dev):
+    """stream= runs the layer on another stream: its outputs and workspace
+    are allocated on that stream, so default-stream allocations made while
+    the kernels run cannot take their memory; results are bitwise those of
+    the default-stream call."""
+    w = STREAM["stream_sigmoid_groups_shared"]
+    inp = to_dev(make_inputs(w, seed=17, device="cpu"), dev)
+    ref = run(w, inp)
+    cfg = moe.MoeConfig.from_workload(w)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        outs.append(moe.moe_layer_forward(inp["u"], inp["W_router"], inp["bias"], inp["W1"], inp["W3"],
+                                          inp["W2"], inp["shared"], cfg=cfg, stream=side))
+        junk = torch.full((w.T * w.k, w.d), 7.0, dtype=inp["u"].dtype, device=dev)
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for out in outs:
+        for a, b in zip(ref, out):
+            assert torch.equal(a, b)
+
+
 def test_zero_tokens_is_a_noop(dev):
     w = SMALL["softmax_bias_bf16"]
     inp = to_dev(make_inputs(w.with_(T=4), seed=5, device="cpu"), dev)
@@ -313,7 +339,11 @@ def test_route_debug_permutation_is_exact(dev, name):
 
 # ------------------------------------------------------------------ full-size workloads
 
-def check_large(w, inp, n_sample, seed=0, must_include=None):
+def check_large(w, inp, n_sample, seed=0, must_include=None, tile_edges=True, tag=None):
+    """Routing of every token against the oracle, and the outputs of n_sample
+    seeded random tokens plus (tile_edges) the tokens in the first and last
+    row of every routed and shared tile the GEMMs ran, from the permutation
+    the library built on the same inputs."""
     u, Wr, bias = oracle_inputs(inp)
     bias_arg = bias if inp["bias"] is not None else None
     log(f"[{w.name}] gpu forward")
@@ -325,17 +355,31 @@ def check_large(w, inp, n_sample, seed=0, must_include=None):
     st = route_parity(w, gi, g.cpu().numpy(), ir, gr, ge, gg, lg, bias)
     rng = np.random.default_rng(seed)
     tok = rng.choice(w.T, size=min(n_sample, w.T), replace=False)
+    n_tiles = 0
+    if tile_edges:
+        cfg = moe.MoeConfig.from_workload(w)
+        path, tile_m = moe.moe_plan_describe(cfg)
+        idx2, _, counts, _, perm, _ = moe.moe_route_debug(inp["u"], inp["W_router"], inp["bias"], cfg=cfg)
+        torch.cuda.synchronize()
+        assert torch.equal(idx2, idx), "the debug entry point routes as the forward does"
+        edge, n_tiles = tile_edge_tokens(w, path, tile_m, counts.cpu().numpy(), perm.cpu().numpy(), w.T)
+        tok = np.concatenate([tok, edge])
+        st["gemm_path"] = path
+        st["tiles"] = int(n_tiles)
+        st["tile_edge_tokens"] = int(edge.size)
     if must_include is not None:
-        tok = np.unique(np.concatenate([tok, must_include]))
+        tok = np.concatenate([tok, must_include])
+    tok = np.unique(tok)
     near = (ge < 1e-5) | (gg < 1e-5)
     sel = np.where(near[tok, None], gi[tok], ir[tok])
-    log(f"[{w.name}] oracle outputs on {tok.size} tokens")
+    log(f"[{w.name}] oracle outputs on {tok.size} tokens ({n_tiles} tiles)")
     yr, _, _ = sampled_outputs(w, inp, tok, sel)
     err = rel_l2(widen_gpu(y[torch.from_numpy(tok).to(y.device)]), yr)
-    assert err.max() <= Y_TOL[w.dtype], f"max rel-L2 {err.max():.3e}"
+    assert err.max() <= Y_TOL[w.dtype], f"max rel-L2 {err.max():.3e} at token {tok[err.argmax()]}"
     st["rel_l2_max"] = float(err.max())
-    st["sampled"] = int(tok.size)
+    st["outputs_checked"] = int(tok.size)
     log(f"[{w.name}] {st}")
+    record(tag or w.name, st)
     return y, idx, g, st
 
 
@@ -350,7 +394,7 @@ def _release_memory():
 def test_mixtral_full_size(dev):
     w = WORKLOADS["mixtral_e8_top2"]
     inp = make_inputs(w, seed=0, device=dev)
-    check_large(w, inp, n_sample=24)
+    check_large(w, inp, n_sample=256)
     del inp
 
 
@@ -374,16 +418,20 @@ def test_dsv3_prefill_and_decode_full_size_packed(dev):
 
 
 def test_dsv3_prefill_full_size(dev):
+    """Every token's routing, and the outputs of 256 random tokens plus the
+    first and last row of each of the ~420 routed and 32 shared tiles."""
     w = WORKLOADS["dsv3_prefill"]
     inp = make_inputs(w, seed=0, device=dev)
-    check_large(w, inp, n_sample=12)
+    check_large(w, inp, n_sample=256)
     del inp
 
 
 def test_dsv3_decode_full_size(dev):
+    """All 64 tokens: routing and outputs."""
     w = WORKLOADS["dsv3_decode"]
     inp = make_inputs(w, seed=0, device=dev)
-    check_large(w, inp, n_sample=24)
+    _, _, _, st = check_large(w, inp, n_sample=w.T)
+    assert st["outputs_checked"] == w.T
     del inp
 
 
@@ -394,7 +442,7 @@ def test_dsv3_full_size_other_seed_plain_and_packed(dev, name, seed):
     equal to the plain one."""
     w = WORKLOADS[name]
     inp = make_inputs(w, seed=seed, device=dev)
-    y, idx, g, _ = check_large(w, inp, n_sample=8, seed=seed)
+    y, idx, g, _ = check_large(w, inp, n_sample=64, seed=seed, tag=f"{name}_seed{seed}")
     cfg = moe.MoeConfig.from_workload(w)
     packed = moe.moe_pack_weights(inp["W1"], inp["W3"], inp["W2"], inp["shared"], cfg=cfg)
     yp, ip, gp = moe.moe_layer_forward_packed(inp["u"], inp["W_router"], inp["bias"], packed, cfg=cfg)
@@ -410,7 +458,7 @@ def test_streaming_schedule_overflow_falls_back_to_the_tiled_kernels(dev):
     w = Workload("huge_t", 720_000, 256, 8, 2, 128, 0, "softmax", 1, 1, 1.0, "bf16", "zero")
     assert moe.moe_plan_describe(moe.MoeConfig.from_workload(w))[0] == "tiled"
     inp = make_inputs(w, seed=4, device=dev)
-    check_large(w, inp, n_sample=16, must_include=np.array([0, w.T - 1]))
+    check_large(w, inp, n_sample=16, must_include=np.array([0, w.T - 1]), tile_edges=False)
     del inp
 
 
@@ -431,13 +479,13 @@ def test_skewed_load_bias_off_and_on(dev):
     log(f"[skewed] alpha={alpha:.4f} expert-0 share at zero bias={share:.4f}")
     assert abs(share - 0.90) <= 0.005
     # bias off
-    _, idx, _, st0 = check_large(w, inp, n_sample=16,
+    _, idx, _, st0 = check_large(w, inp, n_sample=256, tag="skewed_e128_top8_bias_off",
                                  must_include=np.nonzero((idx0 == 0).any(1))[0][:8])
     cnt0 = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.E)
     # bias on: the aux-loss-free loop's correction vector
     b, hist = balance.balance_bias(lg, w.k)
     inp["bias"] = torch.from_numpy(b.astype(np.float32)).to(dev)
-    _, idx, _, st1 = check_large(w, inp, n_sample=16,
+    _, idx, _, st1 = check_large(w, inp, n_sample=256, tag="skewed_e128_top8_bias_on",
                                  must_include=np.nonzero((idx0 == 0).any(1))[0][:8])
     cnt1 = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.E)
     e0, e1 = balance.entropy(cnt0), balance.entropy(cnt1)
