@@ -119,6 +119,30 @@ moe_status moe_layer_forward(const void *u, const void *W_router, const float *b
                              size_t workspace_bytes, void *stream);
 
 /*
+ * moe_layer_forward for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments and results as moe_layer_forward
+ * (bitwise), minus the workspace: the library keeps one fixed device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU (its static storage, held until the
+ * process ends) and uses it as the workspace.  The call itself allocates
+ * nothing and enqueues no memset or copy.
+ *   - Limit: configurations whose workspace (moe_workspace_bytes) exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE before any HIP call
+ *     (64 MiB covers, e.g., the DeepSeek-V3 layer shape up to T = 256).
+ *   - The array of the current device is used; the stream must belong to it.
+ *     Its address is looked up once per device, at the first call there.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (other streams, other threads) race and must be
+ *     serialised by the caller.  Nothing from an earlier call is read.
+ *   - Per-stage timing (moe_timing_enable) does not record these calls.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_layer_forward_noalloc(const void *u, const void *W_router, const float *bias,
+                                     const void *W1, const void *W3, const void *W2,
+                                     const moe_shared *shared, const moe_cfg *cfg, void *y,
+                                     int32_t *topk_idx, float *gates, void *stream);
+
+/*
  * Packed weights (bf16 layers with d, F and F_shared multiples of 256).
  *
  * The expert weights are static, so they may be re-laid out once (model

@@ -108,6 +108,8 @@ def lib():
         L.moe_layer_forward.argtypes = [P, P, P, P, P, P, ctypes.POINTER(moe_shared), CP, P, P, P,
                                         P, SZ, P]
         L.moe_layer_forward.restype = I32
+        L.moe_layer_forward_noalloc.argtypes = [P, P, P, P, P, P, ctypes.POINTER(moe_shared), CP, P, P, P, P]
+        L.moe_layer_forward_noalloc.restype = I32
         L.moe_route_debug.argtypes = [P, P, P, CP, P, P, P, P, P, P, P, SZ, P]
         L.moe_route_debug.restype = I32
         L.moe_balance_update.argtypes = [P, I64, I32, I32, ctypes.c_float, P, P, P, P]
@@ -284,6 +286,44 @@ def moe_layer_forward(u, W_router, bias, W1, W3, W2, shared: Optional[Sequence] 
                                  workspace.numel(), _stream(dev, stream))
     if st != 0:
         raise MoeError(st, "moe_layer_forward")
+    return y, topk_idx, gates
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+@_on_stream
+def moe_layer_forward_noalloc(u, W_router, bias, W1, W3, W2, shared: Optional[Sequence] = None, *,
+                              cfg: MoeConfig, y, topk_idx, gates, stream=None):
+    """moe_layer_forward without a workspace: the library's fixed per-GPU
+    scratch array serves as one.  The outputs y, topk_idx and gates are the
+    caller's (nothing is allocated here either)."""
+    dev = u.device
+    dt = cfg.torch_dtype
+    T, d, E, k, F, Fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.F_shared
+    _need(u, (T, d), dt, "u", dev)
+    _need(W_router, (E, d), dt, "W_router", dev)
+    _need(W1, (E, F, d), dt, "W1", dev)
+    _need(W3, (E, F, d), dt, "W3", dev)
+    _need(W2, (E, d, F), dt, "W2", dev)
+    if bias is not None:
+        _need(bias, (E,), torch.float32, "bias", dev)
+    sh = None
+    if shared is not None:
+        W1s, W3s, W2s = shared
+        _need(W1s, (Fs, d), dt, "W1s", dev)
+        _need(W3s, (Fs, d), dt, "W3s", dev)
+        _need(W2s, (d, Fs), dt, "W2s", dev)
+        sh = moe_shared(W1s.data_ptr(), W3s.data_ptr(), W2s.data_ptr())
+    _need(y, (T, d), dt, "y", dev)
+    _need(topk_idx, (T, k), torch.int32, "topk_idx", dev)
+    _need(gates, (T, k), torch.float32, "gates", dev)
+    c = cfg.to_c()
+    st = lib().moe_layer_forward_noalloc(_ptr(u), _ptr(W_router), _ptr(bias), _ptr(W1), _ptr(W3), _ptr(W2),
+                                         ctypes.byref(sh) if sh is not None else None, ctypes.byref(c),
+                                         _ptr(y), _ptr(topk_idx), _ptr(gates), _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_layer_forward_noalloc")
     return y, topk_idx, gates
 
 

@@ -188,16 +188,24 @@ static moe_status prepare(const moe_cfg *cfg, int kind, void *workspace, size_t 
   return MOE_OK;
 }
 
-// Validation shared by the two forward entry points; *p is filled on success.
-static moe_status check_forward(const void *u, const void *W_router, const moe_cfg *cfg, int kind, const void *y,
-                                const int32_t *topk_idx, const float *gates, void *workspace,
-                                size_t workspace_bytes, Plan *p) {
+// The token input and the outputs of a forward call.
+static moe_status check_io(const void *u, const void *W_router, const moe_cfg *cfg, const void *y,
+                           const int32_t *topk_idx, const float *gates) {
   if (!u || !W_router || !y || !topk_idx || !gates) return MOE_ERR_NULL;
   if (!aligned16(u) || !aligned16(W_router) || !aligned16(y)) return MOE_ERR_ALIGN;
   const size_t bytes = static_cast<size_t>(cfg->T) * cfg->d * (cfg->dtype == MOE_BF16 ? 2 : 4);
   const char *a = static_cast<const char *>(u);
   const char *b = static_cast<const char *>(y);
   if (a < b + bytes && b < a + bytes) return MOE_ERR_SHAPE;  // y aliases u
+  return MOE_OK;
+}
+
+// Validation shared by the forward entry points; *p is filled on success.
+static moe_status check_forward(const void *u, const void *W_router, const moe_cfg *cfg, int kind, const void *y,
+                                const int32_t *topk_idx, const float *gates, void *workspace,
+                                size_t workspace_bytes, Plan *p) {
+  const moe_status st = check_io(u, W_router, cfg, y, topk_idx, gates);
+  if (st != MOE_OK) return st;
   return prepare(cfg, kind, workspace, workspace_bytes, p);
 }
 
@@ -218,13 +226,15 @@ static Experts swiglu_experts(const void *W1, const void *W3, const void *W2, co
 
 // residual: nullptr for the layer, the block input h for the block form.
 // pk: the packed buffer's regions (SwiGLU), or null for x's plain weights.
+// timing: the per-stage timing hooks may run (they create HIP events while
+// timing is enabled); the allocation-free entry point passes false.
 static moe_status run_layer(const Plan &p, const void *u, const void *W_router, const float *bias,
                             const Experts &x, const PackedView *pk, void *y, int32_t *topk_idx, float *gates,
-                            hipStream_t s, const void *residual = nullptr) {
+                            hipStream_t s, const void *residual = nullptr, bool timing = true) {
   (void)hipGetLastError();  // report only errors of the launches below
   Record rec{};
   bool timed = false;
-  {
+  if (timing) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (g_timing && g_records.size() < kMaxRecords) {
       int made = 0;
@@ -269,6 +279,22 @@ static moe_status run_layer(const Plan &p, const void *u, const void *W_router, 
   return MOE_OK;
 }
 
+}  // extern "C"
+
+// The plain SwiGLU weights of moe_layer_forward and its allocation-free twin
+// (checked after cfg, for T > 0).
+static moe_status check_plain_weights(const void *W1, const void *W3, const void *W2, const moe_shared *shared) {
+  if (!W1 || !W3 || !W2) return MOE_ERR_NULL;
+  if (shared && (!shared->W1 || !shared->W3 || !shared->W2)) return MOE_ERR_NULL;
+  const void *ptrs[] = {W1, W3, W2, shared ? shared->W1 : W1, shared ? shared->W3 : W1,
+                        shared ? shared->W2 : W1};
+  for (const void *q : ptrs)
+    if (!aligned16(q)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+extern "C" {
+
 moe_status moe_layer_forward(const void *u, const void *W_router, const float *bias, const void *W1,
                              const void *W3, const void *W2, const moe_shared *shared,
                              const moe_cfg *cfg, void *y, int32_t *topk_idx, float *gates,
@@ -277,17 +303,75 @@ moe_status moe_layer_forward(const void *u, const void *W_router, const float *b
   if (st != MOE_OK) return st;
   if ((cfg->F_shared > 0) != (shared != nullptr)) return MOE_ERR_CFG;
   if (cfg->T == 0) return MOE_OK;
-  if (!W1 || !W3 || !W2) return MOE_ERR_NULL;
-  if (shared && (!shared->W1 || !shared->W3 || !shared->W2)) return MOE_ERR_NULL;
-  const void *ptrs[] = {W1, W3, W2, shared ? shared->W1 : W1, shared ? shared->W3 : W1,
-                        shared ? shared->W2 : W1};
-  for (const void *q : ptrs)
-    if (!aligned16(q)) return MOE_ERR_ALIGN;
+  st = check_plain_weights(W1, W3, W2, shared);
+  if (st != MOE_OK) return st;
   Plan p;
   st = check_forward(u, W_router, cfg, MOE_EXPERT_SWIGLU, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
   return run_layer(p, u, W_router, bias, swiglu_experts(W1, W3, W2, shared), nullptr, y, topk_idx, gates,
                    static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---- allocation-free forward -------------------------------------------------
+
+namespace {
+// The workspace of moe_layer_forward_noalloc: a fixed array in device memory,
+// one copy per GPU the library runs on, held until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: only the
+// address hipGetSymbolAddress returns for the current device is ever passed
+// to a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device with that device current.
+moe_status scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward_noalloc(const void *u, const void *W_router, const float *bias, const void *W1,
+                                     const void *W3, const void *W2, const moe_shared *shared,
+                                     const moe_cfg *cfg, void *y, int32_t *topk_idx, float *gates,
+                                     void *stream) {
+  moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if ((cfg->F_shared > 0) != (shared != nullptr)) return MOE_ERR_CFG;
+  if (cfg->T == 0) return MOE_OK;
+  st = check_plain_weights(W1, W3, W2, shared);
+  if (st == MOE_OK) st = check_io(u, W_router, cfg, y, topk_idx, gates);
+  if (st != MOE_OK) return st;
+  // Argument errors and sizes beyond the array are reported before any HIP call.
+  Plan probe;
+  make_plan(*cfg, MOE_EXPERT_SWIGLU, nullptr, &probe);
+  if (probe.bytes > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != MOE_OK) return st;
+  Plan p;
+  st = check_forward(u, W_router, cfg, MOE_EXPERT_SWIGLU, y, topk_idx, gates, ws, MOE_NOALLOC_SCRATCH_BYTES, &p);
+  if (st != MOE_OK) return st;
+  // Every buffer the kernels read from the scratch is written earlier in the
+  // same call (the GEMM work counters by the schedule kernel), so nothing is
+  // cleared and nothing from an earlier call is read.
+  return run_layer(p, u, W_router, bias, swiglu_experts(W1, W3, W2, shared), nullptr, y, topk_idx, gates,
+                   static_cast<hipStream_t>(stream), nullptr, /*timing=*/false);
 }
 
 }  // extern "C"

@@ -284,3 +284,47 @@ def test_packed_expert_body_sizes_and_argument_checks():
     ex = binding.moe_experts(binding.MOE_EXPERT_GELU_MLP)
     assert L.moe_layer_forward_packed_ex(None, None, None, ctypes.byref(ex), None, ctypes.byref(x0), None, None,
                                          None, None, 0, None) == 0
+
+
+def test_noalloc_forward_refuses_oversized_work_and_bad_arguments_before_any_gpu_call():
+    """moe_layer_forward_noalloc: the same argument checks as moe_layer_forward,
+    and a configuration whose workspace exceeds the fixed per-GPU array is
+    refused with MOE_ERR_WORKSPACE, all before any HIP call (this runs with
+    no GPU)."""
+    L = moe.lib()
+
+    def call(c, **ptrs):
+        # fake, never dereferenced, aligned pointers 1 TiB apart (no overlap at any size here)
+        p = {n: ctypes.c_void_p((i + 1) << 40) for i, n in enumerate(
+            ["u", "Wr", "W1", "W3", "W2", "y", "idx", "gates"])}
+        p.update(ptrs)
+        cc = c.to_c()
+        return L.moe_layer_forward_noalloc(p["u"], p["Wr"], None, p["W1"], p["W3"], p["W2"], None,
+                                           ctypes.byref(cc), p["y"], p["idx"], p["gates"], None)
+
+    assert binding.NOALLOC_SCRATCH_BYTES == 64 << 20
+    big = moe.MoeConfig.from_workload(WORKLOADS["dsv3_prefill"]).to_c()
+    assert moe.moe_workspace_bytes(moe.MoeConfig.from_workload(WORKLOADS["dsv3_prefill"])) > 64 << 20
+    c = cfg(n_groups=1, topk_groups=1)
+    assert moe.moe_workspace_bytes(c) <= 64 << 20
+    big_c = moe.MoeConfig.from_workload(WORKLOADS["dsv3_prefill"].with_(Fs=0))
+    assert call(big_c) == -5                  # workspace beyond MOE_NOALLOC_SCRATCH_BYTES
+    assert call(cfg(n_groups=1, topk_groups=1, T=40000, d=1024, F=1024)) == -5
+    assert call(c, u=None) == -1
+    assert call(c, W2=None) == -1
+    assert call(c, u=ctypes.c_void_p((1 << 40) + 8)) == -7
+    assert call(c, y=ctypes.c_void_p(1 << 40)) == -2   # y aliases u
+    assert call(cfg(T=0)) == 0                          # no-op
+    assert call(cfg(F_shared=128)) == -3                # shared width but no shared weights
+    assert call(cfg(k=17)) == -3
+    del big
+
+
+def test_package_exports_a_python_wrapper_for_every_c_entry_point():
+    # every moe_* function the header declares has a wrapper of the same name in the package,
+    # except the timing and host-only helpers that the wrappers call themselves
+    host_only = {"moe_packed_weights_bytes", "moe_status_str"}
+    for n in declared_functions():
+        if n in host_only:
+            continue
+        assert hasattr(moe, n), n
