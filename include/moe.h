@@ -31,7 +31,10 @@
  * Conventions for every entry point:
  *   - Tensor pointers are device memory owned by the caller, row-major and
  *     contiguous, 16-byte aligned.  The library never allocates device memory
- *     and keeps no state between calls (except the optional timing records).
+ *     at run time.  Host state kept between calls: the optional timing
+ *     records, the CU count of the device (read once), and the device
+ *     address of each GPU's fixed scratch array of moe_layer_forward_noalloc
+ *     (static device storage, looked up once per GPU).
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL for
  *     the default stream); calls return after enqueueing and never
  *     synchronise.  Device faults surface at the caller's next sync.
