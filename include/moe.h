@@ -303,6 +303,37 @@ moe_status moe_block_forward_packed(const void *h, const void *norm_weight, floa
                                     void *stream);
 
 /*
+ * The same block with the normalisation fused into the router and the first
+ * expert product (no pass that writes normalised rows):
+ *   RMSNorm(h)_j = rs * h_j * g_j,  rs = 1 / sqrt(mean_j h_j^2 + eps)
+ * g is static, so it is folded once into the weights that multiply the
+ * normalised rows: W_router, W1, W3, W1s, W3s (each product w * g[j]
+ * rounded once to bf16, nearest even); rs is a per-token scalar, so the
+ * router sums each token's squares in its pass over h (fp32, fixed order),
+ * scales the token's logits by rs before the score function, and the gate/up
+ * GEMM scales its accumulators of that token's rows by rs before SiLU.
+ * Routing decisions are thus taken on rs * (h . bf16(W_router * g)).
+ *
+ * moe_block_packed_bytes: size of the fused block's packed buffer: the
+ *   packed SwiGLU weights (moe_packed_weights_bytes) followed by the folded
+ *   router rows [E][d]; 0 when cfg cannot be packed (bf16, d, F and F_shared
+ *   multiples of 256).
+ * moe_pack_block_weights: fills it from norm_weight [d], W_router and the
+ *   plain expert weights of moe_block_forward (enqueued on stream).
+ * moe_block_forward_fused: y = h + MoE(RMSNorm(h)) from that buffer, as
+ *   moe_block_forward, with workspace_bytes >= moe_block_workspace_bytes(cfg).
+ *   MOE_ERR_SHAPE when cfg cannot be packed or is beyond the streaming
+ *   kernels (see moe_layer_forward_packed); MOE_ERR_CFG for a bad norm_eps.
+ */
+size_t moe_block_packed_bytes(const moe_cfg *cfg);
+moe_status moe_pack_block_weights(const moe_cfg *cfg, const void *norm_weight, const void *W_router,
+                                  const void *W1, const void *W3, const void *W2, const moe_shared *shared,
+                                  void *packed, size_t packed_bytes, void *stream);
+moe_status moe_block_forward_fused(const void *h, float norm_eps, const float *bias, const void *packed,
+                                   const moe_cfg *cfg, void *y, int32_t *topk_idx, float *gates,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One step of the auxiliary-loss-free balance update ("Mixture of Experts and
  * Hybrid Architectures", "Aux-loss-free balance loop"; the bias moves only
  * selection, "Sparse MoE FFN", "How it works", Routing), from the routing of

@@ -124,6 +124,12 @@ def lib():
         L.moe_block_forward.restype = I32
         L.moe_block_forward_packed.argtypes = [P, P, F32, P, P, P, CP, P, P, P, P, SZ, P]
         L.moe_block_forward_packed.restype = I32
+        L.moe_block_packed_bytes.argtypes = [CP]
+        L.moe_block_packed_bytes.restype = SZ
+        L.moe_pack_block_weights.argtypes = [CP, P, P, P, P, P, ctypes.POINTER(moe_shared), P, SZ, P]
+        L.moe_pack_block_weights.restype = I32
+        L.moe_block_forward_fused.argtypes = [P, F32, P, P, CP, P, P, P, P, SZ, P]
+        L.moe_block_forward_fused.restype = I32
         L.moe_packed_weights_bytes.argtypes = [CP]
         L.moe_packed_weights_bytes.restype = SZ
         L.moe_pack_weights.argtypes = [CP, P, P, P, ctypes.POINTER(moe_shared), P, SZ, P]
@@ -636,6 +642,71 @@ def moe_block_forward_packed(h, norm_weight, norm_eps, W_router, bias, packed, *
                                         _ptr(gates), _ptr(workspace), workspace.numel(), _stream(dev, stream))
     if st != 0:
         raise MoeError(st, "moe_block_forward_packed")
+    return y, topk_idx, gates
+
+
+def moe_block_packed_bytes(cfg: MoeConfig) -> int:
+    """Bytes of the fused block's packed buffer (0: cfg cannot be packed)."""
+    c = cfg.to_c()
+    return int(lib().moe_block_packed_bytes(ctypes.byref(c)))
+
+
+@_on_stream
+def moe_pack_block_weights(norm_weight, W_router, W1, W3, W2, shared: Optional[Sequence] = None, *,
+                           cfg: MoeConfig, packed=None, stream=None):
+    """One-time packing for moe_block_forward_fused: the expert weights in the
+    streaming kernels' order with the RMSNorm weight folded into W1, W3 (and
+    the shared W1s, W3s), then the router rows folded the same way."""
+    dev = W1.device
+    dt = cfg.torch_dtype
+    E, d, F, Fs = cfg.E, cfg.d, cfg.F, cfg.F_shared
+    _need(norm_weight, (d,), dt, "norm_weight", dev)
+    _need(W_router, (E, d), dt, "W_router", dev)
+    _need(W1, (E, F, d), dt, "W1", dev)
+    _need(W3, (E, F, d), dt, "W3", dev)
+    _need(W2, (E, d, F), dt, "W2", dev)
+    sh = None
+    if shared is not None:
+        W1s, W3s, W2s = shared
+        _need(W1s, (Fs, d), dt, "W1s", dev)
+        _need(W3s, (Fs, d), dt, "W3s", dev)
+        _need(W2s, (d, Fs), dt, "W2s", dev)
+        sh = moe_shared(W1s.data_ptr(), W3s.data_ptr(), W2s.data_ptr())
+    n = moe_block_packed_bytes(cfg)
+    if n == 0:
+        raise MoeError(-2, "moe_block_packed_bytes")
+    if packed is None:
+        packed = torch.empty(n, dtype=torch.uint8, device=dev)
+    c = cfg.to_c()
+    st = lib().moe_pack_block_weights(ctypes.byref(c), _ptr(norm_weight), _ptr(W_router), _ptr(W1), _ptr(W3),
+                                      _ptr(W2), ctypes.byref(sh) if sh is not None else None, _ptr(packed),
+                                      packed.numel(), _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_pack_block_weights")
+    return packed
+
+
+@_on_stream
+def moe_block_forward_fused(h, norm_eps, bias, packed, *, cfg: MoeConfig, y=None, topk_idx=None, gates=None,
+                            workspace=None, stream=None):
+    """y = h + MoE(RMSNorm(h)) with the normalisation fused (packed buffer from
+    moe_pack_block_weights, which holds the norm weight and the router)."""
+    dev = h.device
+    dt = cfg.torch_dtype
+    T, d, E = cfg.T, cfg.d, cfg.E
+    _need(h, (T, d), dt, "h", dev)
+    if bias is not None:
+        _need(bias, (E,), torch.float32, "bias", dev)
+    _need(packed, (moe_block_packed_bytes(cfg),), torch.uint8, "packed", dev)
+    y, topk_idx, gates = _block_outputs(cfg, dev, y, topk_idx, gates)
+    if workspace is None:
+        workspace = alloc_block_workspace(cfg, dev)
+    c = cfg.to_c()
+    st = lib().moe_block_forward_fused(_ptr(h), float(norm_eps), _ptr(bias), _ptr(packed), ctypes.byref(c),
+                                       _ptr(y), _ptr(topk_idx), _ptr(gates), _ptr(workspace), workspace.numel(),
+                                       _stream(dev, stream))
+    if st != 0:
+        raise MoeError(st, "moe_block_forward_fused")
     return y, topk_idx, gates
 
 

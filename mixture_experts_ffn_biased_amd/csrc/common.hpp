@@ -41,6 +41,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
+// Eight bf16 values times eight bf16 scales: each fp32 product (exact for
+// two bf16 values) rounded once to bf16, nearest even.
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, uint4 g) {
+  const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t b[4] = {g.x, g.y, g.z, g.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = bf16_to_f32(static_cast<uint16_t>(a[i])) * bf16_to_f32(static_cast<uint16_t>(b[i]));
+    const float hi = bf16_to_f32(static_cast<uint16_t>(a[i] >> 16)) * bf16_to_f32(static_cast<uint16_t>(b[i] >> 16));
+    o[i] = pack_bf16x2(lo, hi);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // 4 x 4 transpose within each quad of lanes, to bf16.  Lane j = lane & 3
 // holds f[b] = rows b = 0..3 of its own column (the four lanes of a quad hold
 // four consecutive columns); it returns row (j & 1) * 2 + (j >> 1) of those

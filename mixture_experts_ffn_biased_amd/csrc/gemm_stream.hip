@@ -119,6 +119,10 @@ struct StreamArgs {
   void *C_routed, *C_shared;
   const void *bias_routed;  // [E][N] or null (EPI_BIAS, EPI_BIAS_GELU)
   const void *bias_shared;  // [N] or null
+  // Row scales of the gated first product (fused pre-norm block): the 1/rms
+  // of the row's token at each routed position ([S] + one tile of padding)
+  // and of each token for the shared expert ([T] + padding); null: none.
+  const float *rs_routed, *rs_shared;
 };
 
 template <int NS>
@@ -598,6 +602,13 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   rows_here = rows_here < 0 ? 0 : (rows_here > 128 ? 128 : rows_here);
   const int nmi = VAR == 0 ? __builtin_amdgcn_readfirstlane((rows_here + 31) >> 5) : 1;
 
+  // Row scale of this thread's row of the tile (gated first product of the
+  // fused pre-norm block), loaded now and staged for the epilogue after the
+  // K loop; rows past the tile read the buffer's padding and are never stored.
+  const float *rs_src = DUAL ? (shared ? g.rs_shared : g.rs_routed) : nullptr;
+  float my_rs = 1.f;
+  if (rs_src && tid < BM) my_rs = rs_src[tl.row0 + tid];
+
   // The previous item's stores and loads are complete before the ring refills.
   wait_vmcnt<0>();
   raw_barrier();
@@ -674,12 +685,22 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   using I512 = std::integral_constant<int, 512>;
   if (DUAL) {
     // H tile: BM rows x 128 columns bf16 (256 bytes a row), 128 rows a slot
-    // (pair ring: token slots 0 and 1; stage ring: slots 0 and 1).
+    // (pair ring: token slots 0 and 1; stage ring: slots 0 and 1, the
+    // decode tile's 32 rows in slot 0).  Row scales: weight slot 0 (pair
+    // ring) or slot 2 (stage ring).
     unsigned char *Ht;
-    if constexpr (PAIR)
+    float *rs_lds;
+    if constexpr (PAIR) {
       Ht = wm ? ring.a1 : ring.a0;
-    else
+      rs_lds = reinterpret_cast<float *>(ring.b0);
+    } else {
       Ht = wm ? ring.s[1] : ring.s[0];
+      rs_lds = reinterpret_cast<float *>(ring.s[2]);
+    }
+    if (rs_src) {
+      if (tid < BM) rs_lds[tid] = my_rs;
+      __syncthreads();
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       if (mi >= nmi) break;
@@ -688,8 +709,16 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
         float f[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const float a1 = acc[mi][0][4 * a + b];
-          f[b] = (EPI == EPI_GELU_GLU ? gelu(a1) : silu_fast(a1)) * acc[mi][1][4 * a + b];
+          float a1 = acc[mi][0][4 * a + b];
+          float a3 = acc[mi][1][4 * a + b];
+          if (rs_src) {
+            // accumulator 4a + b is row 8a + 4 (lane / 32) + b of block mi of
+            // this wave's half of the tile (rows wm * 128 ..)
+            const float r = rs_lds[wm * 128 + mi * 32 + 8 * a + row_lane + b];
+            a1 *= r;
+            a3 *= r;
+          }
+          f[b] = (EPI == EPI_GELU_GLU ? gelu(a1) : silu_fast(a1)) * a3;
         }
         const int row = mi * 32 + 8 * a + row_lane + rq;
         *reinterpret_cast<uint2 *>(Ht + staged(row, wn * 32 + cq, 256)) = quad_transpose_bf16(f, jq);
@@ -838,9 +867,13 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_decode(StreamArgs g) {
 // LDS: row r, physical 16-byte chunk p holds k-chunk p ^ ((r>>2)&3) of the
 // K-slice; for gate_up, row r is W1 row slab*128 + (r/64)*32 + r%32 when
 // r%64 < 32 and the same row of W3 otherwise.
+// g (the fused pre-norm block's RMSNorm weight, [K]; null: none): each value
+// is multiplied by g of its column, the fp32 product (exact for two bf16
+// values) rounded once to bf16, nearest even.
 __global__ __launch_bounds__(256) void pack_weights(const uint16_t *__restrict__ W1,
                                                     const uint16_t *__restrict__ W3, int dual,
                                                     int64_t n_mats, int rows, int K,
+                                                    const uint16_t *__restrict__ g,
                                                     uint16_t *__restrict__ out) {
   const int KT = K / SBK;
   const int nslab = dual ? rows / (SBN / 2) : rows / SBN;
@@ -866,8 +899,24 @@ __global__ __launch_bounds__(256) void pack_weights(const uint16_t *__restrict__
       row = static_cast<int64_t>(slab) * SBN + r;
       src = W1;
     }
-    const uint16_t *from = src + (e * rows + row) * K + kt * SBK + c * 8;
-    *reinterpret_cast<uint4 *>(out + q * 8) = *reinterpret_cast<const uint4 *>(from);
+    const int k0 = kt * SBK + c * 8;
+    const uint16_t *from = src + (e * rows + row) * K + k0;
+    uint4 v = *reinterpret_cast<const uint4 *>(from);
+    if (g) v = scale_bf16x8(v, *reinterpret_cast<const uint4 *>(g + k0));
+    *reinterpret_cast<uint4 *>(out + q * 8) = v;
+  }
+}
+
+// Router rows folded with the RMSNorm weight for the fused pre-norm block:
+// out[e][j] = bf16(W[e][j] * g[j]), as in pack_weights; 8 values a thread.
+__global__ __launch_bounds__(256) void fold_rows(const uint16_t *__restrict__ W, const uint16_t *__restrict__ g,
+                                                 int64_t rows, int K, uint16_t *__restrict__ out) {
+  const int64_t n = rows * K / 8;
+  for (int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; q < n;
+       q += static_cast<int64_t>(gridDim.x) * 256) {
+    const int k0 = static_cast<int>((q * 8) % K);
+    const uint4 v = *reinterpret_cast<const uint4 *>(W + q * 8);
+    *reinterpret_cast<uint4 *>(out + q * 8) = scale_bf16x8(v, *reinterpret_cast<const uint4 *>(g + k0));
   }
 }
 
@@ -1039,22 +1088,34 @@ PackedView packed_view(const moe_cfg &c, int kind, const void *base) {
 
 hipError_t launch_pack_weights(const moe_cfg &c, int kind, const void *W1, const void *W3, const void *W2,
                                const void *W1s, const void *W3s, const void *W2s, void *packed,
-                               hipStream_t s) {
+                               hipStream_t s, const void *norm_weight) {
   const PackedView v = packed_view(c, kind, packed);
   const int dual = kind == MOE_EXPERT_GELU_MLP ? 0 : 1;
-  auto run = [&](const void *a, const void *b, int du, int64_t n, int rows, int K, const void *out) {
+  const uint16_t *g = static_cast<const uint16_t *>(norm_weight);
+  auto run = [&](const void *a, const void *b, int du, int64_t n, int rows, int K, const uint16_t *gk,
+                 const void *out) {
     const int64_t chunks = n * static_cast<int64_t>(rows) * K * (du ? 2 : 1) / 8;
     const unsigned blocks = static_cast<unsigned>(chunks / 256 < 65536 ? (chunks + 255) / 256 : 65536);
     hipLaunchKernelGGL(pack_weights, dim3(blocks), dim3(256), 0, s, static_cast<const uint16_t *>(a),
-                       static_cast<const uint16_t *>(b), du, n, rows, K,
+                       static_cast<const uint16_t *>(b), du, n, rows, K, gk,
                        static_cast<uint16_t *>(const_cast<void *>(out)));
     return hipGetLastError();
   };
-  hipError_t e = run(W1, dual ? W3 : nullptr, dual, c.E, c.F, c.d, v.gu);
-  if (e == hipSuccess) e = run(W2, nullptr, 0, c.E, c.d, c.F, v.dn);
-  if (e == hipSuccess && c.F_shared > 0) e = run(W1s, dual ? W3s : nullptr, dual, 1, c.F_shared, c.d, v.gu_s);
-  if (e == hipSuccess && c.F_shared > 0) e = run(W2s, nullptr, 0, 1, c.d, c.F_shared, v.dn_s);
+  // The norm weight scales the inputs of the first product only (K = d).
+  hipError_t e = run(W1, dual ? W3 : nullptr, dual, c.E, c.F, c.d, g, v.gu);
+  if (e == hipSuccess) e = run(W2, nullptr, 0, c.E, c.d, c.F, nullptr, v.dn);
+  if (e == hipSuccess && c.F_shared > 0)
+    e = run(W1s, dual ? W3s : nullptr, dual, 1, c.F_shared, c.d, g, v.gu_s);
+  if (e == hipSuccess && c.F_shared > 0) e = run(W2s, nullptr, 0, 1, c.d, c.F_shared, nullptr, v.dn_s);
   return e;
+}
+
+hipError_t launch_fold_rows(const void *W, const void *norm_weight, int64_t rows, int K, void *out, hipStream_t s) {
+  const int64_t chunks = rows * K / 8;
+  const unsigned blocks = static_cast<unsigned>(chunks / 256 < 65536 ? (chunks + 255) / 256 : 65536);
+  hipLaunchKernelGGL(fold_rows, dim3(blocks), dim3(256), 0, s, static_cast<const uint16_t *>(W),
+                     static_cast<const uint16_t *>(norm_weight), rows, K, static_cast<uint16_t *>(out));
+  return hipGetLastError();
 }
 
 hipError_t launch_stream_schedule(const Plan &p, hipStream_t s) {
@@ -1126,6 +1187,8 @@ hipError_t launch_stream_gate_up(const Plan &p, const void *u, const Experts &x,
   a.K_shared = c.d;
   a.C_routed = p.H;
   a.C_shared = p.Hs;
+  a.rs_routed = p.rperm;  // null unless the plan is the fused pre-norm block's
+  a.rs_shared = p.rscale;
   return launch_stream(p, a, epi, pk != nullptr, s);
 }
 

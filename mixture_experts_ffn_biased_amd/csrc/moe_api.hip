@@ -73,14 +73,17 @@ static bool valid_kind(int kind) {
   return kind == MOE_EXPERT_SWIGLU || kind == MOE_EXPERT_GEGLU || kind == MOE_EXPERT_GELU_MLP;
 }
 
-void make_plan(const moe_cfg &c, int kind, void *base, Plan *p) {
+void make_plan(const moe_cfg &c, int kind, void *base, Plan *p, int fused_norm, float norm_eps) {
   p->cfg = c;
   p->kind = kind;
+  p->fused_norm = fused_norm;
+  p->norm_eps = norm_eps;
   p->S = c.T * c.k;
   p->path = choose_path(c, kind);
   p->tile_m = p->path == PATH_TILED ? gemm_tile_m(c.dtype) : stream_tile_m(p->path);
   p->tile_balanced = p->path == PATH_TILED ? 0 : stream_tile_balanced(p->path);
   p->router_splits = (c.dtype == MOE_BF16 && c.d % 128 == 0) ? router_splits(c.T, c.d) : 1;
+  const bool split_pair = p->router_splits > 1 || fused_norm;  // logits kernel + router_select
   p->n_perm_blocks = (p->S + kPermChunk - 1) / kPermChunk;
   p->max_tiles = (p->S + p->tile_m - 1) / p->tile_m + c.E +
                  (c.F_shared > 0 ? (c.T + p->tile_m - 1) / p->tile_m : 0);
@@ -93,7 +96,7 @@ void make_plan(const moe_cfg &c, int kind, void *base, Plan *p) {
     return ptr;
   };
   p->router_part = static_cast<float *>(
-      take(p->router_splits > 1 ? sizeof(float) * p->router_splits * c.T * c.E : 0));
+      take(split_pair ? sizeof(float) * p->router_splits * c.T * c.E : 0));
   p->blk_counts = static_cast<int32_t *>(take(sizeof(int32_t) * p->n_perm_blocks * c.E));
   p->blk_base = static_cast<int32_t *>(take(sizeof(int32_t) * p->n_perm_blocks * c.E));
   p->counts = static_cast<int32_t *>(take(sizeof(int32_t) * c.E));
@@ -115,6 +118,12 @@ void make_plan(const moe_cfg &c, int kind, void *base, Plan *p) {
   p->Hs = take(es * c.T * c.F_shared);
   p->O = take(es * p->S * c.d);
   p->Z = take(c.F_shared > 0 ? es * c.T * c.d : 0);
+  p->part_sq = p->rscale = p->rperm = nullptr;
+  if (fused_norm) {
+    p->part_sq = static_cast<float *>(take(sizeof(float) * p->router_splits * c.T));
+    p->rscale = static_cast<float *>(take(sizeof(float) * (c.T + 256)));
+    p->rperm = static_cast<float *>(take(sizeof(float) * (p->S + 256)));
+  }
   p->bytes = off;
 }
 
@@ -518,11 +527,16 @@ moe_status moe_layer_forward_packed(const void *u, const void *W_router, const f
 
 static size_t elem_bytes(const moe_cfg &c) { return c.dtype == MOE_BF16 ? 2 : 4; }
 
+// The larger of the two block forms' needs: the layer's buffers plus the
+// normalised rows (unfused), or the layer's buffers with the row-scale
+// buffers of the fused form.
 size_t moe_block_workspace_bytes(const moe_cfg *cfg) {
   if (validate(cfg) != MOE_OK || cfg->d > rmsnorm_max_d()) return 0;
-  Plan p;
+  Plan p, f;
   make_plan(*cfg, MOE_EXPERT_SWIGLU, nullptr, &p);
-  return p.bytes + align_up(static_cast<size_t>(cfg->T) * cfg->d * elem_bytes(*cfg));
+  make_plan(*cfg, MOE_EXPERT_SWIGLU, nullptr, &f, 1);
+  const size_t unfused = p.bytes + align_up(static_cast<size_t>(cfg->T) * cfg->d * elem_bytes(*cfg));
+  return unfused > f.bytes ? unfused : f.bytes;
 }
 
 moe_status moe_rmsnorm(const void *h, const void *norm_weight, float eps, int64_t T, int32_t d, int32_t dtype,
@@ -603,6 +617,64 @@ moe_status moe_block_forward_packed(const void *h, const void *norm_weight, floa
   const PackedView pk = packed_view(*cfg, MOE_EXPERT_SWIGLU, packed);
   return run_layer(p, un, W_router, bias, swiglu_experts(nullptr, nullptr, nullptr, nullptr), &pk, y, topk_idx,
                    gates, s, h);
+}
+
+// ---- pre-norm block with the normalisation fused -----------------------------
+
+size_t moe_block_packed_bytes(const moe_cfg *cfg) {
+  if (validate(cfg) != MOE_OK || !packable(*cfg)) return 0;
+  return packed_weights_bytes(*cfg, MOE_EXPERT_SWIGLU) + static_cast<size_t>(cfg->E) * cfg->d * 2;
+}
+
+moe_status moe_pack_block_weights(const moe_cfg *cfg, const void *norm_weight, const void *W_router, const void *W1,
+                                  const void *W3, const void *W2, const moe_shared *shared, void *packed,
+                                  size_t packed_bytes, void *stream) {
+  moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if (!packable(*cfg)) return MOE_ERR_SHAPE;
+  if ((cfg->F_shared > 0) != (shared != nullptr)) return MOE_ERR_CFG;
+  if (!norm_weight || !W_router || !packed) return MOE_ERR_NULL;
+  st = check_plain_weights(W1, W3, W2, shared);
+  if (st != MOE_OK) return st;
+  if (!aligned16(norm_weight) || !aligned16(W_router) || !aligned16(packed)) return MOE_ERR_ALIGN;
+  if (packed_bytes < moe_block_packed_bytes(cfg)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (launch_pack_weights(*cfg, MOE_EXPERT_SWIGLU, W1, W3, W2, shared ? shared->W1 : nullptr,
+                          shared ? shared->W3 : nullptr, shared ? shared->W2 : nullptr, packed, s,
+                          norm_weight) != hipSuccess)
+    return MOE_ERR_HIP;
+  void *router = static_cast<char *>(packed) + packed_weights_bytes(*cfg, MOE_EXPERT_SWIGLU);
+  if (launch_fold_rows(W_router, norm_weight, cfg->E, cfg->d, router, s) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_block_forward_fused(const void *h, float norm_eps, const float *bias, const void *packed,
+                                   const moe_cfg *cfg, void *y, int32_t *topk_idx, float *gates, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  moe_status st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if (!packable(*cfg)) return MOE_ERR_SHAPE;
+  if (!std::isfinite(norm_eps) || norm_eps < 0.f) return MOE_ERR_CFG;
+  if (cfg->T == 0) return MOE_OK;
+  if (!packed) return MOE_ERR_NULL;
+  if (!aligned16(packed)) return MOE_ERR_ALIGN;
+  const void *router = static_cast<const char *>(packed) + packed_weights_bytes(*cfg, MOE_EXPERT_SWIGLU);
+  st = check_io(h, router, cfg, y, topk_idx, gates);
+  if (st != MOE_OK) return st;
+  Plan probe;
+  make_plan(*cfg, MOE_EXPERT_SWIGLU, nullptr, &probe, 1, norm_eps);
+  if (probe.path == PATH_TILED) return MOE_ERR_SHAPE;  // beyond the streaming kernels' limits
+  if (!workspace) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes < probe.bytes) return MOE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+  Plan p;
+  make_plan(*cfg, MOE_EXPERT_SWIGLU, workspace, &p, 1, norm_eps);
+  const PackedView pk = packed_view(*cfg, MOE_EXPERT_SWIGLU, packed);
+  // The router and the gate/up GEMM read h itself; the norm weight is in the
+  // packed weights and each token's 1/rms comes from the router's pass over h.
+  return run_layer(p, h, router, bias, swiglu_experts(nullptr, nullptr, nullptr, nullptr), &pk, y, topk_idx,
+                   gates, static_cast<hipStream_t>(stream), h);
 }
 
 moe_status moe_balance_update(const int32_t *topk_idx, int64_t T, int32_t k, int32_t E, float gamma,

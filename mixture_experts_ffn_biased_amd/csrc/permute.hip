@@ -113,9 +113,13 @@ __global__ __launch_bounds__(256) void perm_scan(
 // slots of that expert in the earlier waves of the round, plus its rank
 // among the lanes of its own wave holding the same expert.  The lanes with
 // the same expert are found with one ballot per bit of the expert index.
+// rscale (fused pre-norm block; null otherwise): the token's 1/rms is copied
+// to its slot's position, rperm[pos] = rscale[slot / k].
 __global__ __launch_bounds__(256) void perm_scatter(const int32_t *__restrict__ idx, int64_t S, int E,
                                                     const int32_t *__restrict__ blk_base,
-                                                    int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+                                                    int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+                                                    const float *__restrict__ rscale, int k,
+                                                    float *__restrict__ rperm) {
   static_assert(kMaxExperts <= 256, "expert index in 8 bits");
   __shared__ int run[kMaxExperts];
   __shared__ int wcnt[4][kMaxExperts];  // slots of each expert in each wave of the round
@@ -144,6 +148,7 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t *__restrict__ 
       for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
       perm[pos] = static_cast<int32_t>(s);
       inv[s] = pos;
+      if (rscale) rperm[pos] = rscale[s / k];
     }
     __syncthreads();
     for (int ee = tid; ee < E; ee += 256) run[ee] += wcnt[0][ee] + wcnt[1][ee] + wcnt[2][ee] + wcnt[3][ee];
@@ -169,7 +174,7 @@ hipError_t launch_permute(const Plan &p, const int32_t *topk_idx, hipStream_t s)
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(perm_scatter, dim3(nblk), dim3(256), 0, s, topk_idx, p.S, c.E, p.blk_base,
-                     p.perm, p.inv);
+                     p.perm, p.inv, p.rscale, c.k, p.rperm);
   return hipGetLastError();
 }
 

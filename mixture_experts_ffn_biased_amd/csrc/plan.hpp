@@ -109,13 +109,24 @@ struct Plan {
   void *Hs;             // [T][F_shared] same for the shared expert
   void *O;              // [S][d]        expert output of each routed slot
   void *Z;              // [T][d]        shared expert output (layer dtype)
+  // Fused pre-norm block (fused_norm): the router sums each token's squares
+  // (part_sq), router_select stores 1/rms (rscale), the permutation copies it
+  // to each routed row's position (rperm), and the gate/up epilogue scales
+  // the accumulators of that row by it.  Null otherwise.
+  int fused_norm;
+  float norm_eps;
+  float *part_sq;       // [router_splits][T]
+  float *rscale;        // [T] (+ one tile of padding)
+  float *rperm;         // [S] (+ one tile of padding)
   size_t bytes;
 };
 
 moe_status validate(const moe_cfg *c);
 int router_splits(int64_t T, int d);
-// Fills *p for experts of the given kind; base == nullptr computes only the size.
-void make_plan(const moe_cfg &c, int kind, void *base, Plan *p);
+// Fills *p for experts of the given kind; base == nullptr computes only the
+// size.  fused_norm: the plan of the fused pre-norm block (its router always
+// takes the split-K pair and the plan carries the row-scale buffers).
+void make_plan(const moe_cfg &c, int kind, void *base, Plan *p, int fused_norm = 0, float norm_eps = 0.f);
 
 hipError_t launch_router_topk(const Plan &p, const void *u, const void *Wr, const float *bias,
                               int32_t *topk_idx, float *gates, hipStream_t s);
@@ -135,9 +146,13 @@ int stream_nslab_gate_up(int F, int kind);
 int stream_nslab_down(int d);
 size_t packed_weights_bytes(const moe_cfg &c, int kind);
 PackedView packed_view(const moe_cfg &c, int kind, const void *base);
+// norm_weight (bf16 [d]; null: none): the fused pre-norm block's RMSNorm
+// weight, folded into the first product's weights (W1, W3, W1s, W3s).
 hipError_t launch_pack_weights(const moe_cfg &c, int kind, const void *W1, const void *W3, const void *W2,
                                const void *W1s, const void *W3s, const void *W2s, void *packed,
-                               hipStream_t s);
+                               hipStream_t s, const void *norm_weight = nullptr);
+// out [rows][K] = bf16(W * norm_weight[col]) (bf16, rows * K % 8 == 0).
+hipError_t launch_fold_rows(const void *W, const void *norm_weight, int64_t rows, int K, void *out, hipStream_t s);
 hipError_t launch_stream_schedule(const Plan &p, hipStream_t s);
 // pk == nullptr: the plain weights of x; else the packed buffer's regions
 // (x's weight pointers are not read; its biases are).

@@ -401,10 +401,16 @@ __global__ __launch_bounds__(256, 1) void router_topk_stream(
 // tokens over K range s and stores them (fp32); router_select then adds the
 // splits in a fixed order (deterministic) and selects.
 
+//
+// part_sq (fused pre-norm block; null otherwise): each workgroup also sums
+// the squares of its 64 tokens' inputs over its K range, in fp32 from the
+// same LDS fragments the MFMAs read (wave w squares fragment mi = w/2 of
+// half kk = w%2, so every value is squared exactly once), and stores them
+// at part_sq[split][t]; router_select turns the sums into 1/rms.
 template <int NB>
 __global__ __launch_bounds__(256, 2) void router_logits_split(
     const uint16_t *__restrict__ u, const uint16_t *__restrict__ Wr, int64_t T, int d, int E,
-    int kt_per_split, float *__restrict__ part) {
+    int kt_per_split, float *__restrict__ part, float *__restrict__ part_sq) {
   constexpr int A_B = kRowsS * 64;
   constexpr int B_B = NB * 64 * 64;
   constexpr int SLOT = A_B + B_B;
@@ -454,6 +460,9 @@ __global__ __launch_bounds__(256, 2) void router_logits_split(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
   const int wcol = wave < NB ? wave : 0;
+  const bool want_sq = part_sq != nullptr;
+  const int sq_mi = wave >> 1, sq_kk = wave & 1;
+  float sq = 0.f;  // squares of row sq_mi * 32 + lane % 32, this lane's K values
   auto compute = [&](const unsigned char *st) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -469,6 +478,14 @@ __global__ __launch_bounds__(256, 2) void router_logits_split(
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+      if (want_sq && kk == sq_kk) {
+        const bf16x8 v = sq_mi ? a[1] : a[0];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = static_cast<float>(v[i]);
+          sq = fmaf(x, x, sq);  // x * x is exact in fp32
+        }
+      }
     }
   };
   const int KT = kt_per_split;  // multiple of 4, >= 4
@@ -515,6 +532,21 @@ __global__ __launch_bounds__(256, 2) void router_logits_split(
           if (col < E && t < T) __builtin_nontemporal_store(acc[mi][ni][r], &out[t * E + col]);
         }
   }
+  if (want_sq) {
+    // Row r's squares: waves 2(r/32) and 2(r/32)+1 (the two K halves), lanes
+    // r%32 and r%32+32 of each, added in that fixed order.  Ring slot 0 is
+    // free: every wave has passed the barrier after its last read of it.
+    float *sqs = reinterpret_cast<float *>(ring0);
+    sqs[wave * 64 + lane] = sq;
+    __syncthreads();
+    if (tid < kRowsS) {
+      const int mi = tid >> 5, l = tid & 31;
+      const float *w0 = sqs + (2 * mi) * 64, *w1 = sqs + (2 * mi + 1) * 64;
+      const float v = (w0[l] + w0[l + 32]) + (w1[l] + w1[l + 32]);
+      const int64_t t = t0 + tid;
+      if (t < T) part_sq[static_cast<int64_t>(split) * T + t] = v;
+    }
+  }
 }
 
 // One wave per token: logits = sum of the splits in order, then selection.
@@ -523,11 +555,17 @@ __global__ __launch_bounds__(256, 2) void router_logits_split(
 // past the last split re-read it and add +0, which changes nothing), so the
 // partial sums cost one memory round trip, not one per split.  The sum order
 // is fixed: four running sums over splits sp % 4, then (v0 + v1) + (v2 + v3).
+//
+// Fused pre-norm block (part_sq non-null): the token's sum of squares is the
+// splits' partial sums added in order; rs = 1 / sqrt(sum / d + eps) (IEEE
+// square root and division) scales the summed logits before selection, and
+// is stored at rscale[t] for the gate/up epilogue.
 template <int NSC>
 __global__ __launch_bounds__(256) void router_select(const float *__restrict__ part, int nsplit,
                                                      int64_t T, SelArgs sel,
                                                      int32_t *__restrict__ topk_idx,
-                                                     float *__restrict__ gates) {
+                                                     float *__restrict__ gates, const float *__restrict__ part_sq,
+                                                     int d, float eps, float *__restrict__ rscale) {
   __shared__ float lg[4][kLogitStride];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = sel.E;
@@ -544,13 +582,21 @@ __global__ __launch_bounds__(256) void router_select(const float *__restrict__ p
       x[p][sp] = __builtin_nontemporal_load(&part[(static_cast<int64_t>(spc) * T + t) * E + e]);
     }
   }
+  float rs = 1.f;
+  if (part_sq) {
+    float q = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) q += part_sq[static_cast<int64_t>(sp) * T + t];
+    rs = 1.0f / sqrtf(q / static_cast<float>(d) + eps);
+    if (lane == 0) rscale[t] = rs;
+  }
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int e = lane + 64 * p;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sp = 0; sp < NSC; ++sp) v[sp & 3] += sp < nsplit ? x[p][sp] : 0.f;
-    if (e < E) lg[wave][e] = (v[0] + v[1]) + (v[2] + v[3]);
+    const float l = (v[0] + v[1]) + (v[2] + v[3]);
+    if (e < E) lg[wave][e] = part_sq ? rs * l : l;
   }
   select_token(lg[wave], sel, topk_idx + t * sel.k, gates + t * sel.k);
 }
@@ -571,7 +617,9 @@ hipError_t launch_router_topk(const Plan &p, const void *u, const void *Wr, cons
                               int32_t *topk_idx, float *gates, hipStream_t s) {
   const moe_cfg &c = p.cfg;
   SelArgs sel{c.E, c.k, c.score_fn, c.n_groups, c.topk_groups, c.route_scale, bias};
-  if (c.dtype == MOE_BF16 && c.d % 128 == 0 && p.router_splits > 1) {
+  // The fused pre-norm block always takes the split-K pair (its logits
+  // kernel also sums the squares of the token rows), with one split or more.
+  if (c.dtype == MOE_BF16 && c.d % 128 == 0 && (p.router_splits > 1 || p.fused_norm)) {
     const int S = p.router_splits;
     const dim3 grid(static_cast<unsigned>((c.T + kRowsS - 1) / kRowsS), static_cast<unsigned>(S));
     const int ktps = c.d / 32 / S;
@@ -579,24 +627,32 @@ hipError_t launch_router_topk(const Plan &p, const void *u, const void *Wr, cons
     auto *W = static_cast<const uint16_t *>(Wr);
     const int nb = (c.E + 63) / 64;
     if (nb == 1)
-      hipLaunchKernelGGL(router_logits_split<1>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part);
+      hipLaunchKernelGGL(router_logits_split<1>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part,
+                         p.part_sq);
     else if (nb == 2)
-      hipLaunchKernelGGL(router_logits_split<2>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part);
+      hipLaunchKernelGGL(router_logits_split<2>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part,
+                         p.part_sq);
     else if (nb == 3)
-      hipLaunchKernelGGL(router_logits_split<3>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part);
+      hipLaunchKernelGGL(router_logits_split<3>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part,
+                         p.part_sq);
     else
-      hipLaunchKernelGGL(router_logits_split<4>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part);
+      hipLaunchKernelGGL(router_logits_split<4>, grid, dim3(256), 0, s, U, W, c.T, c.d, c.E, ktps, p.router_part,
+                         p.part_sq);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const dim3 sgrid(static_cast<unsigned>((c.T + 3) / 4));
     if (S <= 4)
-      hipLaunchKernelGGL(router_select<4>, sgrid, dim3(256), 0, s, p.router_part, S, c.T, sel, topk_idx, gates);
+      hipLaunchKernelGGL(router_select<4>, sgrid, dim3(256), 0, s, p.router_part, S, c.T, sel, topk_idx, gates,
+                         p.part_sq, c.d, p.norm_eps, p.rscale);
     else if (S <= 8)
-      hipLaunchKernelGGL(router_select<8>, sgrid, dim3(256), 0, s, p.router_part, S, c.T, sel, topk_idx, gates);
+      hipLaunchKernelGGL(router_select<8>, sgrid, dim3(256), 0, s, p.router_part, S, c.T, sel, topk_idx, gates,
+                         p.part_sq, c.d, p.norm_eps, p.rscale);
     else if (S <= 12)
-      hipLaunchKernelGGL(router_select<12>, sgrid, dim3(256), 0, s, p.router_part, S, c.T, sel, topk_idx, gates);
+      hipLaunchKernelGGL(router_select<12>, sgrid, dim3(256), 0, s, p.router_part, S, c.T, sel, topk_idx, gates,
+                         p.part_sq, c.d, p.norm_eps, p.rscale);
     else
-      hipLaunchKernelGGL(router_select<16>, sgrid, dim3(256), 0, s, p.router_part, S, c.T, sel, topk_idx, gates);
+      hipLaunchKernelGGL(router_select<16>, sgrid, dim3(256), 0, s, p.router_part, S, c.T, sel, topk_idx, gates,
+                         p.part_sq, c.d, p.norm_eps, p.rscale);
     return hipGetLastError();
   }
   if (c.dtype == MOE_BF16 && c.d % 128 == 0) {

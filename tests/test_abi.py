@@ -328,3 +328,39 @@ def test_package_exports_a_python_wrapper_for_every_c_entry_point():
         if n in host_only:
             continue
         assert hasattr(moe, n), n
+
+
+def test_fused_block_arguments_are_checked_before_any_launch():
+    L = moe.lib()
+    c = cfg(d=256, F=256, F_shared=256, n_groups=4, topk_groups=2)
+    assert moe.moe_block_packed_bytes(c) == 2 * (3 * 16 * 256 * 256 + 3 * 256 * 256) + 16 * 256 * 2
+    assert moe.moe_block_packed_bytes(cfg(d=192)) == 0          # not packable
+    assert moe.moe_block_workspace_bytes(c) >= moe.moe_workspace_bytes(c)
+    P = {n: ctypes.c_void_p((i + 1) << 40) for i, n in enumerate(["h", "pk", "y", "idx", "g", "ws"])}
+
+    def fwd(cc, eps=1e-6, ws_bytes=1 << 40, **kw):
+        p = dict(P, **kw)
+        x = cc.to_c()
+        return L.moe_block_forward_fused(p["h"], eps, None, p["pk"], ctypes.byref(x), p["y"], p["idx"], p["g"],
+                                         p["ws"], ws_bytes, None)
+    assert fwd(c, eps=-1.0) == -3
+    assert fwd(c, eps=float("nan")) == -3
+    assert fwd(cfg(d=192)) == -2
+    assert fwd(c, pk=None) == -1
+    assert fwd(c, h=None) == -1
+    assert fwd(c, pk=ctypes.c_void_p((2 << 40) + 4)) == -7
+    assert fwd(c, ws_bytes=16) == -5
+    assert fwd(c, ws=None) == -5
+    assert fwd(cfg(d=256, F=256, F_shared=256, T=0)) == 0
+    sh = binding.moe_shared(1 << 41, 1 << 42, 1 << 43)
+
+    def pack(cc, **kw):
+        p = {n: ctypes.c_void_p((i + 1) << 40) for i, n in enumerate(["g", "Wr", "W1", "W3", "W2", "pk"])}
+        p.update(kw)
+        x = cc.to_c()
+        return L.moe_pack_block_weights(ctypes.byref(x), p["g"], p["Wr"], p["W1"], p["W3"], p["W2"],
+                                        ctypes.byref(sh), p["pk"], kw.get("nbytes", 1 << 40), None)
+    assert pack(c, g=None) == -1
+    assert pack(c, Wr=None) == -1
+    assert pack(c, nbytes=16) == -5
+    assert pack(cfg(d=192, F_shared=256)) == -2

@@ -556,3 +556,124 @@ def test_block_residual_passes_through_when_the_experts_output_zero():
     y, idx, g, _, _ = block.block_forward(h, np.ones(d), 1e-6, Wr, W1, W3, W2, 2)
     y0, idx0, g0, _, _ = oracle.forward(block.rmsnorm(h, np.ones(d), 1e-6), Wr, W1, W3, W2, 2)
     assert np.array_equal(idx, idx0) and np.array_equal(y, y0 + h)
+
+
+def _bf16_bits(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+def test_bf16_rounding_is_torchs_nearest_even():
+    """The fused block's fold of the norm weight into the router rows rounds
+    products of two bf16 values to bf16, nearest even: checked against
+    PyTorch's bf16 conversion on products, exact halfway cases and signs."""
+    from oracle import block
+    rng = np.random.default_rng(31)
+    a = oracle.widen(_bf16_bits(rng.standard_normal(4000)))
+    b = oracle.widen(_bf16_bits(1 + 0.1 * rng.standard_normal(4000)))
+    p = a * b  # exact in fp64 and in fp32
+    want = torch.from_numpy(p.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(block.bf16_round(p), want)
+    ties = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 2.0 ** -130 * 3])
+    assert np.array_equal(block.bf16_round(ties),
+                          torch.from_numpy(ties.astype(np.float32)).to(torch.bfloat16).double().numpy())
+    assert block.bf16_round(np.array([1.0 + 2 ** -8]))[0] == 1.0          # tie to the even neighbour
+    assert block.bf16_round(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
+
+
+def _fused_inputs(rng, T=40, d=64, E=16, F=32, Fs=32):
+    h = _bf16_bits(rng.standard_normal((T, d)) * np.exp(rng.standard_normal((T, 1))))
+    Wr = _bf16_bits(rng.standard_normal((E, d)) / math.sqrt(d))
+    W1 = _bf16_bits(rng.standard_normal((E, F, d)) / math.sqrt(d))
+    W3 = _bf16_bits(rng.standard_normal((E, F, d)) / math.sqrt(d))
+    W2 = _bf16_bits(rng.standard_normal((E, d, F)) / math.sqrt(F))
+    shared = (_bf16_bits(rng.standard_normal((Fs, d)) / math.sqrt(d)),
+              _bf16_bits(rng.standard_normal((Fs, d)) / math.sqrt(d)),
+              _bf16_bits(rng.standard_normal((d, Fs)) / math.sqrt(Fs)))
+    return h, Wr, W1, W3, W2, shared
+
+
+DSV3_SMALL = dict(score_fn=oracle.SIGMOID, n_groups=4, topk_groups=2, route_scale=2.5)
+
+
+def test_expert_sum_is_the_layers_weighted_sum():
+    """The fused block's output composition, shared + sum_j g_j FFN_j, equals
+    the layer oracle's output for the layer's own selection and gates."""
+    from oracle import block
+    rng = np.random.default_rng(32)
+    h, Wr, W1, W3, W2, shared = _fused_inputs(rng)
+    bias = rng.uniform(-0.05, 0.05, 16)
+    y, idx, g, _, _ = oracle.forward(h, Wr, W1, W3, W2, 4, bias=bias, shared=shared, **DSV3_SMALL)
+    ys = block.expert_sum(h, W1, W3, W2, idx, g, shared)
+    np.testing.assert_allclose(ys, y, rtol=1e-12, atol=1e-13)
+    lg = oracle.router_logits(h, Wr)
+    np.testing.assert_allclose(block.gates_of(lg, idx, oracle.SIGMOID, 2.5), g, rtol=1e-14)
+    ys2, idx2, g2, _, _ = oracle.forward(h, Wr, W1, W3, W2, 3)
+    np.testing.assert_allclose(block.gates_of(oracle.router_logits(h, Wr), idx2, oracle.SOFTMAX, 1.0), g2,
+                               rtol=1e-14)
+
+
+def test_fused_block_with_unit_norm_weight_is_the_block():
+    """g = 1: folding changes nothing (the router rows are already bf16), so
+    the fused block routes as the block on its exact fp64 normalised rows and
+    returns the same output."""
+    from oracle import block
+    rng = np.random.default_rng(33)
+    h, Wr, W1, W3, W2, shared = _fused_inputs(rng)
+    g = _bf16_bits(np.ones(h.shape[1]))
+    bias = rng.uniform(-0.05, 0.05, 16)
+    kw = dict(bias=bias, shared=shared, **DSV3_SMALL)
+    y, idx, gt, ge, gg = block.fused_block_forward(h, g, 1e-6, Wr, W1, W3, W2, 4, **kw)
+    y0, idx0, g0, ge0, gg0 = block.block_forward(h, g, 1e-6, Wr, W1, W3, W2, 4, **kw)
+    assert np.array_equal(idx, idx0)
+    np.testing.assert_allclose(gt, g0, rtol=1e-13)
+    np.testing.assert_allclose(y, y0, rtol=1e-12, atol=1e-12)
+
+
+def test_fused_block_with_a_power_of_two_norm_weight_routes_as_the_block():
+    """g = 2 everywhere: W_router * g is exact in bf16, so the fused routing
+    equals the block's on RMSNorm(h) = 2 h / rms, and so does the output."""
+    from oracle import block
+    rng = np.random.default_rng(34)
+    h, Wr, W1, W3, W2, shared = _fused_inputs(rng)
+    g = _bf16_bits(np.full(h.shape[1], 2.0))
+    kw = dict(shared=shared, score_fn=oracle.SOFTMAX)
+    y, idx, gt, _, _ = block.fused_block_forward(h, g, 1e-6, Wr, W1, W3, W2, 3, **kw)
+    y0, idx0, g0, _, _ = block.block_forward(h, g, 1e-6, Wr, W1, W3, W2, 3, **kw)
+    assert np.array_equal(idx, idx0)
+    np.testing.assert_allclose(gt, g0, rtol=1e-12)
+    np.testing.assert_allclose(y, y0, rtol=1e-12, atol=1e-12)
+
+
+def test_fused_block_is_invariant_to_the_scale_of_its_input():
+    """RMSNorm(c h) = RMSNorm(h) (eps = 0): with c a power of two, routing is
+    unchanged and the output moves by exactly the residual's change."""
+    from oracle import block
+    rng = np.random.default_rng(35)
+    h, Wr, W1, W3, W2, shared = _fused_inputs(rng)
+    g = _bf16_bits(1 + 0.1 * rng.standard_normal(h.shape[1]))
+    kw = dict(shared=shared, **DSV3_SMALL)
+    y, idx, gt, _, _ = block.fused_block_forward(h, g, 0.0, Wr, W1, W3, W2, 4, **kw)
+    h4 = _bf16_bits(4.0 * oracle.widen(h))
+    y4, idx4, g4, _, _ = block.fused_block_forward(h4, g, 0.0, Wr, W1, W3, W2, 4, **kw)
+    assert np.array_equal(idx, idx4)
+    np.testing.assert_allclose(g4, gt, rtol=1e-13)
+    np.testing.assert_allclose(y4 - oracle.widen(h4), y - oracle.widen(h), rtol=1e-11, atol=1e-12)
+
+
+def test_fused_routing_decides_on_the_bf16_folded_router():
+    """The fused routing's logits are rs * (h . bf16(W_router * g)): against a
+    brute-force sum over the folded rows in exact rational arithmetic for a
+    few tokens."""
+    from oracle import block
+    rng = np.random.default_rng(36)
+    h, Wr, _, _, _, _ = _fused_inputs(rng, T=3, d=16, E=4)
+    g = _bf16_bits(1 + 0.1 * rng.standard_normal(16))
+    _, _, _, _, lg = block.fused_route(h, g, 1e-6, Wr, 2)
+    hw, Ww, gw = oracle.widen(h), oracle.widen(Wr), oracle.widen(g)
+    Wg = block.bf16_round(Ww * gw)
+    for t in range(3):
+        rs = 1.0 / math.sqrt(float(np.mean(hw[t] ** 2)) + 1e-6)
+        for e in range(4):
+            dot = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(hw[t], Wg[e]))
+            assert lg[t, e] == pytest.approx(rs * float(dot), rel=1e-13, abs=1e-15)
