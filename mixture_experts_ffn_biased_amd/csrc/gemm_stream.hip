@@ -285,7 +285,7 @@ struct PPtrs {
 };
 
 // Token load j of wave w fills rows (4w + j) * 8 + l/8 of a token slot, lane
-// l in physical chunk l%8, which holds logical chunk (l%8) ^ (row & 7).  A
+// l in physical chunk l%8, which holds logical chunk (l%8) ^ ((row >> 1) & 7).  A
 // weight load fills 16 rows of 64 B: lane l in row +l/4, physical chunk l%4,
 // holding logical chunk (l%4) ^ ((row>>2)&3).
 template <int EPI, bool PACKED>
@@ -304,7 +304,7 @@ __device__ __forceinline__ PPtrs prefill_ptrs(const StreamArgs &g, const Tile &t
   for (int j = 0; j < V<0>::PA_LOADS; ++j) {
     const int r = (wave * V<0>::PA_LOADS + j) * 8 + (lane >> 3);
     const int rr = r < tl.nrows ? r : 0;  // rows past the count read row 0 (never stored)
-    const uint32_t chunk = static_cast<uint32_t>(((lane & 7) ^ (r & 7)) * 16);
+    const uint32_t chunk = static_cast<uint32_t>(((lane & 7) ^ ((r >> 1) & 7)) * 16);
     const int64_t arow = (g.gather && !shared) ? g.perm[tl.row0 + rr] / g.k : static_cast<int64_t>(tl.row0) + rr;
     p.set_ao(j, static_cast<uint32_t>(arow * K * 2) + chunk);
   }
@@ -362,7 +362,10 @@ __device__ __forceinline__ PPtrs prefill_ptrs(const StreamArgs &g, const Tile &t
 // covers 8 rows x 128 B, whole cache lines of the gathered token rows, where
 // 32-wide slices would cover 16 half lines; weight slots hold one stage, 256
 // rows x 32 K values, as in the stage ring.  Row r of a token slot keeps its
-// logical 16-byte chunk c in physical chunk c ^ (r & 7).
+// logical 16-byte chunk c in physical chunk c ^ ((r >> 1) & 7): the LDS's 64
+// banks span 256 bytes, two slot rows, and a 16-byte read serves 16 lanes a
+// cycle, so the 16 rows a fragment read's lane group touches (8 row pairs)
+// must put one chunk in 8 different bank groups of each row parity.
 struct PRing {
   unsigned char *a0, *a1, *a2;
   unsigned char *b0, *b1, *b2, *b3;
@@ -585,9 +588,9 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   const int sw = (lane >> 2) & 3;
   const int fo0 = (lane & 31) * 64 + (((0 + (lane >> 5)) ^ sw) << 4);
   const int fo1 = (lane & 31) * 64 + (((2 + (lane >> 5)) ^ sw) << 4);
-  // Prefill token fragment: row lane%32 (row & 7 == lane & 7), logical chunk
-  // 4 * half + 2 * kk + lane/32; the K loop XORs in the static part.
-  const int xa = (lane & 31) * (SBKA * 2) + (((lane >> 5) ^ (lane & 7)) << 4);
+  // Prefill token fragment: row lane%32 (so (row >> 1) & 7 == (lane >> 1) & 7),
+  // logical chunk 4 * half + 2 * kk + lane/32; the K loop XORs in the static part.
+  const int xa = (lane & 31) * (SBKA * 2) + (((lane >> 5) ^ ((lane >> 1) & 7)) << 4);
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -607,7 +610,7 @@ __device__ __forceinline__ void run_item(const StreamArgs &g, int2 item, const R
   // K loop; rows past the tile read the buffer's padding and are never stored.
   const float *rs_src = DUAL ? (shared ? g.rs_shared : g.rs_routed) : nullptr;
   float my_rs = 1.f;
-  if (rs_src && tid < BM) my_rs = rs_src[tl.row0 + tid];
+  if (rs_src && tid < tl.nrows) my_rs = rs_src[tl.row0 + tid];
 
   // The previous item's stores and loads are complete before the ring refills.
   wait_vmcnt<0>();
