@@ -61,6 +61,8 @@ def parse():
                     help="skip the informational timings of the GEGLU and GELU-MLP expert bodies")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the decode layer replayed from a captured HIP graph")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the timings of the pre-norm residual block (fused and unfused)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB three times (a plain "
                          "copy kernel of known size, to scale hardware byte counters)")
@@ -536,7 +538,7 @@ def main():
     # the layer inside its pre-norm residual block: y = u + MoE(RMSNorm(u)), with the
     # normalisation fused into the router and gate/up (norm weight folded into a
     # packed buffer once, not timed), and unfused (a separate RMSNorm pass)
-    if packed is not None:
+    if packed is not None and not args.no_block:
         from synthetic import make_norm_weight
         g = make_norm_weight(w, seed=args.seed, device=dev)
         bws = moe.alloc_block_workspace(cfg, dev)
