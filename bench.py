@@ -321,6 +321,16 @@ def other_configs(args, torch, dev):
     import mixture_experts_ffn_biased_amd as moe
     from synthetic import EP_SHARD, WORKLOADS, make_inputs
     out = {}
+    # the tiny fp32 layer (tiled kernels, plain weights): a latency figure
+    w = WORKLOADS["tiny_fp32"]
+    log(f"[bench] {w.name}")
+    inp = make_inputs(w, seed=args.seed, device=dev)
+    ms, _, stage_ms, idx, _ = run_layer(w, inp, inp["u"], 100, args.warmup, torch, None)
+    rec = layer_record(w, ms, stage_ms, int(torch.unique(idx).numel()), moe.moe_plan_describe(
+        moe.MoeConfig.from_workload(w))[0])
+    rec.update(weights="plain", latency_us=round(ms * 1e3, 2))
+    out[w.name] = rec
+    del inp
     w = WORKLOADS["mixtral_e8_top2"]
     log(f"[bench] {w.name}")
     inp = make_inputs(w, seed=args.seed, device=dev)
