@@ -242,16 +242,41 @@ def layer_record(w, ms, stage_ms, hit, path):
 
 
 def time_shape(w, inp, steps, warmup, torch, bias=None):
-    """Pack the shape's weights, time the packed layer, free the weights' copy."""
+    """Pack the shape's weights, time the packed layer, free the weights' copy.
+    Returns the record, the routing and the outputs (y, topk_idx, gates) of
+    the last timed call."""
     import mixture_experts_ffn_biased_amd as moe
     cfg = moe.MoeConfig.from_workload(w)
     packed = moe.moe_pack_weights(inp["W1"], inp["W3"], inp["W2"], inp["shared"], cfg=cfg)
     if bias is not None:
         inp = dict(inp, bias=bias)
-    ms, _, stage_ms, idx, _ = run_layer(w, inp, inp["u"], steps, warmup, torch, packed)
+    ms, _, stage_ms, idx, (y, gates) = run_layer(w, inp, inp["u"], steps, warmup, torch, packed)
     hit = int(torch.unique(idx).numel())
     del packed
-    return layer_record(w, ms, stage_ms, hit, moe.moe_plan_describe(cfg)[0]), idx
+    return layer_record(w, ms, stage_ms, hit, moe.moe_plan_describe(cfg)[0]), idx, (y, idx, gates)
+
+
+def oracle_leg(w, inp, out, n_tokens, seed, bias=None):
+    """The CPU oracle on a bounded sample of one extra shape (part of the CPU
+    baseline leg): routing of every token and the outputs of n_tokens seeded
+    tokens (all when T <= n_tokens), its rate on the host cores, and the
+    parity of the GPU's outputs `out` (y, topk_idx, gates) on that sample."""
+    import numpy as np
+
+    import oracle
+    from synthetic import to_numpy
+    threads = oracle.default_threads()
+    b = inp["bias"] if bias is None else bias
+    tok = np.sort(np.random.default_rng(seed).choice(w.T, size=min(n_tokens, w.T), replace=False))
+    W = (to_numpy(inp["W1"]), to_numpy(inp["W3"]), to_numpy(inp["W2"]),
+         None if inp["shared"] is None else tuple(to_numpy(x) for x in inp["shared"]))
+    par, t_route, t_ffn = oracle_check(w, to_numpy(inp["u"]), to_numpy(inp["W_router"]),
+                                       b.double().cpu().numpy(), W, np.arange(w.E), to_numpy(out[0]),
+                                       out[1].cpu().numpy().astype(np.int64), out[2].cpu().numpy(), tok, threads)
+    n = tok.size
+    rate = {"value": n / (t_ffn + t_route * n / w.T), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"routing of all {w.T} tokens ({t_route:.2f} s) + outputs of {n} seeded tokens ({t_ffn:.2f} s)"}
+    return rate, par
 
 
 def skew_inputs(w, seed, dev, torch, target=0.90):
@@ -321,32 +346,43 @@ def other_configs(args, torch, dev):
     import mixture_experts_ffn_biased_amd as moe
     from synthetic import EP_SHARD, WORKLOADS, make_inputs
     out = {}
+    cpu = not args.no_cpu_baseline
+
+    def cpu_leg(rec, w, inp, res, n, bias=None):
+        # the oracle on a bounded sample, outside every timed region
+        if cpu:
+            rec["cpu_oracle"], rec["parity"] = oracle_leg(w, inp, res, n, args.seed, bias)
+
     # the tiny fp32 layer (tiled kernels, plain weights): a latency figure
     w = WORKLOADS["tiny_fp32"]
     log(f"[bench] {w.name}")
     inp = make_inputs(w, seed=args.seed, device=dev)
-    ms, _, stage_ms, idx, _ = run_layer(w, inp, inp["u"], 100, args.warmup, torch, None)
+    ms, _, stage_ms, idx, (y, gates) = run_layer(w, inp, inp["u"], 100, args.warmup, torch, None)
     rec = layer_record(w, ms, stage_ms, int(torch.unique(idx).numel()), moe.moe_plan_describe(
         moe.MoeConfig.from_workload(w))[0])
     rec.update(weights="plain", latency_us=round(ms * 1e3, 2))
+    cpu_leg(rec, w, inp, (y, idx, gates), w.T)
     out[w.name] = rec
     del inp
     w = WORKLOADS["mixtral_e8_top2"]
     log(f"[bench] {w.name}")
     inp = make_inputs(w, seed=args.seed, device=dev)
-    out[w.name], _ = time_shape(w, inp, args.steps, args.warmup, torch)
-    del inp
+    out[w.name], _, res = time_shape(w, inp, args.steps, args.warmup, torch)
+    cpu_leg(out[w.name], w, inp, res, 64)
+    del inp, res
     w = EP_SHARD
     log(f"[bench] {w.name}")
     inp = make_inputs(w, seed=args.seed, device=dev)
-    out[w.name], _ = time_shape(w, inp, args.steps, args.warmup, torch)
+    out[w.name], _, _ = time_shape(w, inp, args.steps, args.warmup, torch)
     del inp
     w = WORKLOADS["skewed_e128_top8"]
     log(f"[bench] {w.name}: calibrating the skew on the library's routing")
     inp, alpha, got = skew_inputs(w, args.seed, dev, torch)
-    rec_a, idx = time_shape(w, inp, args.steps, args.warmup, torch)
+    rec_a, idx, res = time_shape(w, inp, args.steps, args.warmup, torch)
     rec_a.update(bias="zero", expert0_scale=round(alpha, 4), expert0_share=round(got, 4),
                  expert0_rows=int((idx == 0).sum().item()))
+    cpu_leg(rec_a, w, inp, res, 256)
+    del res
     # the aux-loss-free balance loop on the device: 10 steps of +-0.15 from zero
     cfg = moe.MoeConfig.from_workload(w)
     ws = moe.alloc_workspace(cfg, dev)
@@ -354,9 +390,11 @@ def other_configs(args, torch, dev):
     for _ in range(10):
         idx = moe.moe_route_debug(inp["u"], inp["W_router"], b, cfg=cfg, workspace=ws)[0]
         moe.moe_balance_update(idx, b, E=w.E, gamma=0.15)
-    rec_b, idx = time_shape(w, inp, args.steps, args.warmup, torch, bias=b)
+    rec_b, idx, res = time_shape(w, inp, args.steps, args.warmup, torch, bias=b)
     rec_b.update(bias="10 on-device balance steps, gamma 0.15",
                  expert0_rows=int((idx == 0).sum().item()))
+    cpu_leg(rec_b, w, inp, res, 256, bias=b)
+    del res
     out[w.name + "_a"] = rec_a
     out[w.name + "_b"] = rec_b
     del inp, ws
