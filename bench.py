@@ -509,20 +509,26 @@ def cpu_baseline(w, inp, n_tokens, seed, gpu_out, edge_tok, decode=None):
                                        gpu_out[2].cpu().numpy(), tok, threads)
     par["tile_edge_tokens"] = int(edge_tok.size)
     parity = {w.name: par}
+    decode_rate = None
     n = tok.size
     value = n / (t_ffn + t_route * n / w.T)
     if decode is not None:
         wd, ud, yd, idd, gd = decode
-        pd, _, _ = oracle_check(wd, to_numpy(ud), Wr, bias, W, used, to_numpy(yd),
-                                idd.cpu().numpy().astype(np.int64), gd.cpu().numpy(), np.arange(wd.T), threads)
+        pd, td_route, td_ffn = oracle_check(wd, to_numpy(ud), Wr, bias, W, used, to_numpy(yd),
+                                            idd.cpu().numpy().astype(np.int64), gd.cpu().numpy(),
+                                            np.arange(wd.T), threads)
         parity[wd.name] = pd
+        decode_rate = {"value": wd.T / (td_route + td_ffn), "unit": "tokens/s", "cores": threads,
+                       "kind": "oracle",
+                       "sample": (f"{wd.name}: routing ({td_route:.2f} s) and expert and shared outputs "
+                                  f"({td_ffn:.2f} s) of all {wd.T} tokens")}
     base = {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"{w.name}: routing of all {w.T} tokens ({t_route:.2f} s) + expert and "
                        f"shared outputs of {n} tokens: the {edge_tok.size} in the first or last row of a "
                        f"GEMM tile and seeded random ones ({t_ffn:.2f} s); tokens/s = "
                        f"n / (t_ffn + t_route * n / T); device-to-host copy of the weights "
                        f"({t_copy:.2f} s) excluded")}
-    return base, parity
+    return base, parity, decode_rate
 
 
 def main():
@@ -691,8 +697,10 @@ def main():
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens, parity of the timed outputs")
         edge = tile_edge_tokens(w, inp, inp["u"], torch)
         dec = None if args.no_decode else (wd, ud, yd_out, didx, gd_out)
-        result["cpu_baseline"], result["parity"] = cpu_baseline(
+        result["cpu_baseline"], result["parity"], decode_rate = cpu_baseline(
             w, inp, args.cpu_tokens, args.seed, (y_out, idx, g_out), edge, decode=dec)
+        if decode_rate is not None:
+            result["decode"]["cpu_oracle"] = decode_rate
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
