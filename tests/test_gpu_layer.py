@@ -285,6 +285,60 @@ def test_nan_row_gives_valid_distinct_indices(dev):
     assert gi[7].tolist() == ir[7].tolist()
 
 
+# Routed row counts at and around the tile edges.  Prefill (256-row tiles,
+# rows spread evenly over ceil(c / 256) tiles): 255/256/257 (one tile, one,
+# two), 511/512/513 (two, two, three), 767/768/769 (three, three, four), and
+# counts of 1-2, 31-33, 128-129.  Decode (32-row tiles, ragged last tile):
+# 31/32/33 .. 127/128, counts of 1-3 and 16-17, and 48 experts with no rows.
+TILE_EDGES = {
+    "prefill": (Workload("tile_edges_prefill", 2482, 256, 16, 2, 256, 256, "softmax", 1, 1, 1.0, "bf16",
+                         "zero"),
+                [255, 256, 257, 511, 512, 513, 767, 768, 769, 1, 2, 31, 32, 33, 128, 129], "stream"),
+    "decode": (Workload("tile_edges_decode", 435, 512, 64, 2, 256, 256, "softmax", 1, 1, 1.0, "bf16", "zero"),
+               [31, 32, 33, 63, 64, 65, 95, 96, 97, 1, 2, 3, 16, 17, 127, 128], "stream_decode"),
+}
+
+
+def routed_to_counts(w, counts, seed, dev):
+    """Inputs whose routing gives expert e exactly counts[e] rows: the router
+    reads u's first E columns (W_router is the identity there), and token t's
+    two experts get 8 and 7 in those columns, the others |x| < 0.5, so every
+    selection has a gap of more than 6 at the k-th expert.  Experts come from
+    the sorted slot list: token t takes its t-th and (T + t)-th entries, which
+    differ because no count exceeds T."""
+    assert w.k == 2 and sum(counts) == w.T * w.k and max(counts) < w.T
+    inp = make_inputs(w, seed=seed, device="cpu")
+    slots = np.repeat(np.arange(len(counts)), counts)
+    first, second = slots[:w.T], slots[w.T:]
+    assert (first != second).all()
+    rng = np.random.default_rng(seed)
+    u = inp["u"].float().numpy().copy()
+    u[:, :w.E] = rng.uniform(-0.5, 0.5, size=(w.T, w.E))
+    u[np.arange(w.T), first] = 8.0
+    u[np.arange(w.T), second] = 7.0
+    inp["u"] = torch.from_numpy(u).to(torch.bfloat16)
+    Wr = torch.zeros(w.E, w.d)
+    Wr[torch.arange(w.E), torch.arange(w.E)] = 1.0
+    inp["W_router"] = Wr.to(torch.bfloat16)
+    inp["bias"] = torch.zeros(w.E)
+    return to_dev(inp, dev)
+
+
+@pytest.mark.parametrize("name", list(TILE_EDGES))
+def test_tile_edge_row_counts_every_token(dev, name):
+    w, counts, path = TILE_EDGES[name]
+    assert moe.moe_plan_describe(moe.MoeConfig.from_workload(w))[0] == path
+    log(f"[tile-edges] {name}")
+    inp = routed_to_counts(w, counts, 21, dev)
+    y, idx, g = run(w, inp)
+    got = np.bincount(idx.cpu().numpy().ravel(), minlength=w.E)
+    want = np.zeros(w.E, dtype=np.int64)
+    want[:len(counts)] = counts
+    assert (got == want).all(), f"rows per expert {got.tolist()}"
+    st = check_full(w, inp, y, idx, g)
+    log(f"[tile-edges] {name} {st}")
+
+
 def test_side_stream_call_matches_the_default_stream(dev):
     """stream= runs the layer on another stream: its outputs and workspace
     are allocated on that stream, so default-stream allocations made while
