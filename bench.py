@@ -146,13 +146,17 @@ def layer_bytes(w, hit, s=2):
             + 8 * w.T * w.k)
 
 
-def timed_steps(step, steps, warmup, torch):
+def timed_steps(step, steps, warmup, torch, stage_events=True):
+    """Warm-up calls, then `steps` calls between two events.  With
+    stage_events the library's per-stage events are recorded in the same
+    timed region (the kernel durations the roofline uses); without, nothing
+    but the layer calls is in it."""
     import mixture_experts_ffn_biased_amd as moe
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     moe.moe_timing_read(reset=True)
-    moe.moe_timing_enable(True)
+    moe.moe_timing_enable(stage_events)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -168,7 +172,7 @@ def timed_steps(step, steps, warmup, torch):
     return ms, wall, [s / max(calls, 1) for s in stage_ms], calls
 
 
-def run_layer(w, inp, u, steps, warmup, torch, packed=None):
+def run_layer(w, inp, u, steps, warmup, torch, packed=None, stage_events=True):
     """Time `steps` layer calls (plain weights, or the packed buffer if given)."""
     import mixture_experts_ffn_biased_amd as moe
     cfg = moe.MoeConfig.from_workload(w)
@@ -187,7 +191,7 @@ def run_layer(w, inp, u, steps, warmup, torch, packed=None):
                                   inp["shared"], cfg=cfg, y=y, topk_idx=idx, gates=gates,
                                   workspace=ws)
 
-    ms, wall, stage_ms, calls = timed_steps(step, steps, warmup, torch)
+    ms, wall, stage_ms, calls = timed_steps(step, steps, warmup, torch, stage_events)
     return ms, wall, stage_ms, idx, (y, gates)
 
 
@@ -203,8 +207,12 @@ def graph_ms(w, inp, u, packed, steps, torch):
     ws = moe.alloc_workspace(cfg, dev)
 
     def step():
-        moe.moe_layer_forward_packed(u, inp["W_router"], inp["bias"], packed, cfg=cfg, y=y, topk_idx=idx,
-                                     gates=gates, workspace=ws)
+        if packed is not None:
+            moe.moe_layer_forward_packed(u, inp["W_router"], inp["bias"], packed, cfg=cfg, y=y, topk_idx=idx,
+                                         gates=gates, workspace=ws)
+        else:
+            moe.moe_layer_forward(u, inp["W_router"], inp["bias"], inp["W1"], inp["W3"], inp["W2"],
+                                  inp["shared"], cfg=cfg, y=y, topk_idx=idx, gates=gates, workspace=ws)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -360,7 +368,13 @@ def other_configs(args, torch, dev):
     ms, _, stage_ms, idx, (y, gates) = run_layer(w, inp, inp["u"], 100, args.warmup, torch, None)
     rec = layer_record(w, ms, stage_ms, int(torch.unique(idx).numel()), moe.moe_plan_describe(
         moe.MoeConfig.from_workload(w))[0])
-    rec.update(weights="plain", latency_us=round(ms * 1e3, 2))
+    # the latency without the per-stage events in the timed region, and replayed from a captured graph
+    # (no per-call launch work on the host)
+    ms_plain = run_layer(w, inp, inp["u"], 100, args.warmup, torch, None, stage_events=False)[0]
+    rec.update(weights="plain", latency_us=round(ms_plain * 1e3, 2),
+               latency_us_with_stage_events=round(ms * 1e3, 2))
+    if not args.no_graph:
+        rec["graph_replay_latency_us"] = round(graph_ms(w, inp, inp["u"], None, 100, torch) * 1e3, 2)
     cpu_leg(rec, w, inp, (y, idx, gates), w.T)
     out[w.name] = rec
     del inp
