@@ -363,7 +363,10 @@ moe_status moe_balance_update(const int32_t *topk_idx, int64_t T, int32_t k, int
  * per expert on average, T * d * 2 and max(F, F_shared) * d * 2 below 2^32
  * bytes, which they address with 32-bit offsets), 2 for their decode variant
  * with 32-row tiles (fewer rows per expert; also F % 256 == 0,
- * F_shared % 256 == 0); both also need T within the streaming schedule;
+ * F_shared % 256 == 0; T * d * 2 below 2^32 too); both also need T within
+ * the streaming schedule; 3 for the one-kernel small layer (fp32 SwiGLU,
+ * T * k <= 512, d, F and F_shared <= 1024: one workgroup per token computes
+ * its routing, experts and sum without the permutation or grouped GEMMs);
  * *tile_rows = rows per GEMM tile.  Either pointer may be NULL.
  */
 moe_status moe_plan_describe(const moe_cfg *cfg, int32_t *gemm_path, int32_t *tile_rows);

@@ -172,7 +172,7 @@ def moe_check_cfg(cfg: MoeConfig) -> int:
     return int(lib().moe_check_cfg(ctypes.byref(c)))
 
 
-GEMM_PATHS = {0: "tiled", 1: "stream", 2: "stream_decode"}
+GEMM_PATHS = {0: "tiled", 1: "stream", 2: "stream_decode", 3: "small"}
 
 
 def moe_plan_describe(cfg: MoeConfig):

@@ -43,8 +43,10 @@ static size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 // F % 256, F_shared % 256).  With at least 64 routed rows per expert on
 // average they run 256-row tiles (prefill); with fewer, 32-row tiles with a
 // deeper weight ring (decode), which also needs F % 256 and F_shared % 256.
-// Everything else takes the tiled kernels.
+// Everything else takes the tiled kernels, except small fp32 SwiGLU layers,
+// which run whole in one kernel (small_layer.hip).
 static int choose_path(const moe_cfg &c, int kind) {
+  if (small_layer_fits(c, kind)) return PATH_SMALL;
   if (c.dtype != MOE_BF16) return PATH_TILED;
   if (c.d % 256 != 0 || c.F % 128 != 0 || c.F_shared % 128 != 0) return PATH_TILED;
   if (kind == MOE_EXPERT_GELU_MLP && (c.F % 256 != 0 || c.F_shared % 256 != 0)) return PATH_TILED;
@@ -80,8 +82,9 @@ void make_plan(const moe_cfg &c, int kind, void *base, Plan *p, int fused_norm, 
   p->norm_eps = norm_eps;
   p->S = c.T * c.k;
   p->path = choose_path(c, kind);
-  p->tile_m = p->path == PATH_TILED ? gemm_tile_m(c.dtype) : stream_tile_m(p->path);
-  p->tile_balanced = p->path == PATH_TILED ? 0 : stream_tile_balanced(p->path);
+  const bool streaming = streaming_path(p->path);
+  p->tile_m = streaming ? stream_tile_m(p->path) : gemm_tile_m(c.dtype);
+  p->tile_balanced = streaming ? stream_tile_balanced(p->path) : 0;
   p->router_splits = (c.dtype == MOE_BF16 && c.d % 128 == 0) ? router_splits(c.T, c.d) : 1;
   const bool split_pair = p->router_splits > 1 || fused_norm;  // logits kernel + router_select
   p->n_perm_blocks = (p->S + kPermChunk - 1) / kPermChunk;
@@ -106,7 +109,7 @@ void make_plan(const moe_cfg &c, int kind, void *base, Plan *p, int fused_norm, 
   p->tiles = static_cast<Tile *>(take(sizeof(Tile) * p->max_tiles));
   p->tile_count = static_cast<int32_t *>(take(sizeof(int32_t)));
   p->max_items_gu = p->max_items_dn = 0;
-  if (p->path != PATH_TILED) {
+  if (streaming) {
     const int64_t nslab = stream_nslab_gate_up(c.F > c.F_shared ? c.F : c.F_shared, kind);
     p->max_items_gu = p->max_tiles * nslab;
     p->max_items_dn = p->max_tiles * stream_nslab_down(c.d);
@@ -269,6 +272,16 @@ static moe_status run_layer(const Plan &p, const void *u, const void *W_router, 
     return MOE_ERR_HIP;
   };
   mark(0);
+  if (p.path == PATH_SMALL) {
+    // one kernel: its whole time is the first stage's
+    if (launch_small_layer(p, u, W_router, bias, x, residual, y, topk_idx, gates, s) != hipSuccess) return fail();
+    for (int i = 1; i <= MOE_N_STAGES; ++i) mark(i);
+    if (timed) {
+      std::lock_guard<std::mutex> lk(g_mu);
+      g_records.push_back(rec);
+    }
+    return MOE_OK;
+  }
   if (launch_router_topk(p, u, W_router, bias, topk_idx, gates, s) != hipSuccess) return fail();
   mark(1);
   if (launch_permute(p, topk_idx, s) != hipSuccess) return fail();
@@ -469,7 +482,7 @@ moe_status moe_layer_forward_packed_ex(const void *u, const void *W_router, cons
   Plan p;
   st = check_forward(u, W_router, cfg, x.kind, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
-  if (p.path == PATH_TILED) return MOE_ERR_SHAPE;  // beyond the streaming kernels' limits
+  if (!streaming_path(p.path)) return MOE_ERR_SHAPE;  // beyond the streaming kernels' limits
   const PackedView pk = packed_view(*cfg, x.kind, packed);
   return run_layer(p, u, W_router, bias, x, &pk, y, topk_idx, gates, static_cast<hipStream_t>(stream));
 }
@@ -516,7 +529,7 @@ moe_status moe_layer_forward_packed(const void *u, const void *W_router, const f
   Plan p;
   st = check_forward(u, W_router, cfg, MOE_EXPERT_SWIGLU, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
-  if (p.path == PATH_TILED) return MOE_ERR_SHAPE;  // beyond the streaming kernels' limits
+  if (!streaming_path(p.path)) return MOE_ERR_SHAPE;  // beyond the streaming kernels' limits
   const PackedView pk = packed_view(*cfg, MOE_EXPERT_SWIGLU, packed);
   // The shared expert is present iff F_shared > 0 (the kernels read pk).
   return run_layer(p, u, W_router, bias, swiglu_experts(nullptr, nullptr, nullptr, nullptr), &pk, y, topk_idx,
@@ -606,7 +619,7 @@ moe_status moe_block_forward_packed(const void *h, const void *norm_weight, floa
   Plan p;
   st = check_forward(h, W_router, cfg, MOE_EXPERT_SWIGLU, y, topk_idx, gates, workspace, workspace_bytes, &p);
   if (st != MOE_OK) return st;
-  if (p.path == PATH_TILED) return MOE_ERR_SHAPE;
+  if (!streaming_path(p.path)) return MOE_ERR_SHAPE;
   void *un = nullptr;
   st = block_setup(norm_weight, norm_eps, cfg, p, workspace, workspace_bytes, &un);
   if (st != MOE_OK) return st;
@@ -664,7 +677,7 @@ moe_status moe_block_forward_fused(const void *h, float norm_eps, const float *b
   if (st != MOE_OK) return st;
   Plan probe;
   make_plan(*cfg, MOE_EXPERT_SWIGLU, nullptr, &probe, 1, norm_eps);
-  if (probe.path == PATH_TILED) return MOE_ERR_SHAPE;  // beyond the streaming kernels' limits
+  if (!streaming_path(probe.path)) return MOE_ERR_SHAPE;  // beyond the streaming kernels' limits
   if (!workspace) return MOE_ERR_WORKSPACE;
   if (workspace_bytes < probe.bytes) return MOE_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MOE_ERR_ALIGN;

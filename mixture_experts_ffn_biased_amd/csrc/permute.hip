@@ -169,7 +169,7 @@ hipError_t launch_permute(const Plan &p, const int32_t *topk_idx, hipStream_t s)
                      p.tiles, p.tile_count);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (p.path != PATH_TILED) {
+  if (streaming_path(p.path)) {
     err = launch_stream_schedule(p, s);
     if (err != hipSuccess) return err;
   }

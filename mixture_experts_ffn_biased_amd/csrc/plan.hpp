@@ -46,7 +46,15 @@ enum GemmPath {
   PATH_TILED = 0,          // grouped_gemm.hip: 128-row tiles (fp32 too), any size multiple of 64
   PATH_STREAM = 1,         // gemm_stream.hip prefill variant: 256-row tiles
   PATH_STREAM_DECODE = 2,  // gemm_stream.hip decode variant: 32-row tiles, deep weight ring
+  PATH_SMALL = 3,          // small_layer.hip: the whole small fp32 SwiGLU layer in one kernel
 };
+
+inline bool streaming_path(int path) { return path == PATH_STREAM || path == PATH_STREAM_DECODE; }
+
+// Limits of the one-kernel small layer (fp32, SwiGLU): routed slots, d, F and F_shared.
+constexpr int kSmallMaxSlots = 512;
+constexpr int kSmallMaxD = 1024;
+constexpr int kSmallMaxF = 1024;
 
 // Expert weights of one call in the plain layout and the body they form
 // (moe_expert_kind).  W3 / W3s are unused by the GELU MLP; b1, b2, b1s, b2s
@@ -128,6 +136,10 @@ int router_splits(int64_t T, int d);
 // takes the split-K pair and the plan carries the row-scale buffers).
 void make_plan(const moe_cfg &c, int kind, void *base, Plan *p, int fused_norm = 0, float norm_eps = 0.f);
 
+bool small_layer_fits(const moe_cfg &c, int kind);
+hipError_t launch_small_layer(const Plan &p, const void *u, const void *W_router, const float *bias,
+                              const Experts &x, const void *residual, void *y, int32_t *topk_idx, float *gates,
+                              hipStream_t s);
 hipError_t launch_router_topk(const Plan &p, const void *u, const void *Wr, const float *bias,
                               int32_t *topk_idx, float *gates, hipStream_t s);
 hipError_t launch_permute(const Plan &p, const int32_t *topk_idx, hipStream_t s);

@@ -91,12 +91,25 @@ def test_workspace_grows_with_tokens_and_shared_expert():
 def test_gemm_path_selection():
     from synthetic import WORKLOADS
     path = {n: moe.moe_plan_describe(moe.MoeConfig.from_workload(w))[0] for n, w in WORKLOADS.items()}
-    assert path["tiny_fp32"] == "tiled"
+    assert path["tiny_fp32"] == "small"
     assert path["dsv3_prefill"] == "stream" and path["mixtral_e8_top2"] == "stream"
     assert path["skewed_e128_top8"] == "stream"
     assert path["dsv3_decode"] == "stream_decode"
     assert moe.moe_plan_describe(cfg(d=192))[0] == "tiled"
     assert moe.moe_plan_describe(cfg(T=8, n_groups=1, topk_groups=1))[0] == "tiled"
+
+
+def test_small_fp32_layers_run_in_one_kernel_within_its_limits():
+    # fp32 SwiGLU with T * k <= 512 and d, F, F_shared <= 1024 take the one-kernel path
+    f32 = dict(dtype="f32", E=8, k=2, n_groups=1, topk_groups=1)
+    assert moe.moe_plan_describe(cfg(T=256, d=1024, F=1024, F_shared=1024, **f32))[0] == "small"
+    assert moe.moe_plan_describe(cfg(T=257, d=64, F=128, **f32))[0] == "tiled"   # 514 slots
+    assert moe.moe_plan_describe(cfg(T=64, d=1088, F=128, **f32))[0] == "tiled"
+    assert moe.moe_plan_describe(cfg(T=64, d=64, F=1088, **f32))[0] == "tiled"
+    assert moe.moe_plan_describe(cfg(T=64, d=64, F=128, F_shared=1088, **f32))[0] == "tiled"
+    assert moe.moe_plan_describe_ex(cfg(T=64, d=64, F=128, **f32), "geglu")[0] == "tiled"
+    assert moe.moe_plan_describe(cfg(T=64, d=64, F=128, dtype="bf16", E=8, k=2, n_groups=1,
+                                     topk_groups=1))[0] == "tiled"
 
 
 def test_prefill_stream_needs_a_token_matrix_below_4_gib():

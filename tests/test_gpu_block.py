@@ -33,6 +33,9 @@ SMALL = {
     "sigmoid_groups_shared_bf16": Workload("sigmoid_groups_shared_bf16", 333, 256, 16, 4, 192, 128,
                                            "sigmoid", 4, 2, 2.5, "bf16", "uniform"),
     "tiny_fp32": WORKLOADS["tiny_fp32"],
+    # fp32 beyond the one-kernel small layer (1332 slots): the tiled kernels
+    "sigmoid_groups_shared_fp32": Workload("sigmoid_groups_shared_fp32", 333, 256, 16, 4, 192, 128,
+                                           "sigmoid", 4, 2, 2.5, "f32", "uniform"),
     "stream_sigmoid_groups_shared": Workload("stream_sigmoid_groups_shared", 1200, 512, 16, 4, 384, 256,
                                              "sigmoid", 4, 2, 2.5, "bf16", "uniform"),
     "decode_sigmoid_groups_shared": Workload("decode_sigmoid_groups_shared", 40, 256, 16, 4, 256, 256,

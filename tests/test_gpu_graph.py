@@ -26,6 +26,9 @@ SHAPES = {
     # tiled fp32 kernels (plain weights)
     "tiled_fp32": (Workload("tiled_fp32", 200, 128, 16, 3, 128, 64, "sigmoid", 4, 2, 2.5, "f32", "uniform"),
                    "tiled", False),
+    # the one-kernel small fp32 layer
+    "small_fp32": (Workload("small_fp32", 100, 128, 16, 3, 128, 64, "sigmoid", 4, 2, 2.5, "f32", "uniform"),
+                   "small", False),
 }
 
 

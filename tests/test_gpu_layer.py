@@ -106,6 +106,14 @@ SMALL = {
     # the largest group count (64 groups of 4, keep 8)
     "groups64_sigmoid_bf16": Workload("groups64_sigmoid_bf16", 120, 128, 256, 16, 64, 64, "sigmoid", 64, 8,
                                       2.5, "bf16", "uniform"),
+    # the one-kernel small fp32 layer: groups and a shared expert (510 slots),
+    # its size limits (512 slots, d = F = F_shared = 1024), every expert chosen
+    "small_fp32_groups_shared": Workload("small_fp32_groups_shared", 170, 256, 16, 3, 192, 128, "sigmoid", 4,
+                                         2, 2.5, "f32", "uniform"),
+    "small_fp32_limits": Workload("small_fp32_limits", 256, 1024, 8, 2, 1024, 1024, "softmax", 1, 1, 1.0,
+                                  "f32", "uniform"),
+    "small_fp32_k_equals_E": Workload("small_fp32_k_equals_E", 50, 64, 8, 8, 64, 0, "softmax", 1, 1, 1.0,
+                                      "f32", "zero"),
 }
 
 
@@ -235,9 +243,13 @@ def test_packed_weights_give_bitwise_identical_layer(dev, name):
     check_full(w, inp, *got)
 
 
+SMALL_PATH = {"tiny_fp32", "small_fp32_groups_shared", "small_fp32_limits", "small_fp32_k_equals_E"}
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_layer_every_token(dev, name):
     w = SMALL[name]
+    assert (moe.moe_plan_describe(moe.MoeConfig.from_workload(w))[0] == "small") == (name in SMALL_PATH)
     log(f"[small] {name}")
     inp = to_dev(make_inputs(w, seed=1, device="cpu"), dev)
     y, idx, g = run(w, inp)
