@@ -365,12 +365,12 @@ def other_configs(args, torch, dev):
     w = WORKLOADS["tiny_fp32"]
     log(f"[bench] {w.name}")
     inp = make_inputs(w, seed=args.seed, device=dev)
+    # timed without the per-stage events in the timed region (at this size they would be most of it), the
+    # stage split from a second run with them; and replayed from a captured graph (no per-call launch work)
     ms, _, stage_ms, idx, (y, gates) = run_layer(w, inp, inp["u"], 100, args.warmup, torch, None)
-    rec = layer_record(w, ms, stage_ms, int(torch.unique(idx).numel()), moe.moe_plan_describe(
-        moe.MoeConfig.from_workload(w))[0])
-    # the latency without the per-stage events in the timed region, and replayed from a captured graph
-    # (no per-call launch work on the host)
     ms_plain = run_layer(w, inp, inp["u"], 100, args.warmup, torch, None, stage_events=False)[0]
+    rec = layer_record(w, ms_plain, stage_ms, int(torch.unique(idx).numel()), moe.moe_plan_describe(
+        moe.MoeConfig.from_workload(w))[0])
     rec.update(weights="plain", latency_us=round(ms_plain * 1e3, 2),
                latency_us_with_stage_events=round(ms * 1e3, 2))
     if not args.no_graph:
