@@ -167,7 +167,7 @@ moe_status moe_layer_forward_noalloc(const void *u, const void *W_router, const 
  *   cfg->F_shared > 0).  Returns MOE_ERR_SHAPE when cfg cannot be packed or
  *   is beyond the streaming kernels (moe_plan_describe then reports the
  *   tiled kernels): T too large for the streaming schedule, or a token
- *   matrix u of 4 GiB or more in the prefill variant.
+ *   matrix u of 4 GiB or more.
  */
 size_t moe_packed_weights_bytes(const moe_cfg *cfg);
 moe_status moe_pack_weights(const moe_cfg *cfg, const void *W1, const void *W3, const void *W2,
@@ -254,7 +254,9 @@ moe_status moe_layer_forward_packed_ex(const void *u, const void *W_router, cons
 
 /*
  * Routing and permutation only (the first two stages of moe_layer_forward,
- * same kernels), for tests and tools.  Outputs, all int32 device arrays:
+ * same kernels; the small fp32 layers that moe_layer_forward runs in one
+ * kernel make the same selection there), for tests and tools.  Outputs, all
+ * int32 device arrays:
  *   counts [E]       slots that chose expert e
  *   offsets [E+1]    exclusive prefix sum of counts; offsets[E] = T*k
  *   perm [T*k]       slot (t*k + j) at each expert-contiguous position; within
