@@ -559,3 +559,73 @@ def test_skewed_load_bias_off_and_on(dev):
         f"(ln E = {math.log(w.E):.4f})")
     assert cnt1[0] < cnt0[0] and e1 > e0
     del inp
+
+
+def _divisors(n):
+    return [g for g in range(1, n + 1) if n % g == 0]
+
+
+def random_shapes(n=25, seed=2024):
+    """Seeded random layers over every kernel path (five of each): the
+    one-kernel small fp32 layer, the tiled kernels in fp32 and bf16, and the
+    prefill and decode streaming kernels, with random E, k, d, F, F_shared,
+    score function, groups and bias."""
+    rng = np.random.default_rng(seed)
+    # kind of shape drawn -> the path name the library reports for it
+    kinds = {"small": "small", "tiled_f32": "tiled", "tiled_bf16": "tiled", "stream": "stream",
+             "stream_decode": "stream_decode"}
+    order = list(kinds)
+    out = {}
+    i = 0
+    while len(out) < n:
+        kind = order[len(out) % len(order)]
+        i += 1
+        assert i <= 20 * n, f"random shapes: no {kind} layer drawn in {i} tries"
+        sigmoid = bool(rng.integers(0, 2))
+        if kind == "small":
+            E = int(rng.choice([4, 8, 16, 32])); dtype = "f32"
+            d = 64 * int(rng.integers(1, 9)); F = 64 * int(rng.integers(1, 9)); Fs = 64 * int(rng.integers(0, 4))
+        elif kind == "tiled_f32":
+            E = int(rng.choice([4, 8, 16])); dtype = "f32"
+            d = 64 * int(rng.integers(1, 5)); F = 64 * int(rng.integers(1, 5)); Fs = 64 * int(rng.integers(0, 3))
+        elif kind == "tiled_bf16":
+            E = int(rng.choice([8, 16, 32])); dtype = "bf16"
+            d = 64 * int(rng.choice([1, 3, 5, 7])); F = 64 * int(rng.integers(1, 6)); Fs = 64 * int(rng.integers(0, 3))
+        elif kind == "stream":
+            E = int(rng.choice([8, 16])); dtype = "bf16"
+            d = 256 * int(rng.integers(1, 3)); F = 128 * int(rng.integers(1, 5)); Fs = 128 * int(rng.integers(0, 3))
+        else:
+            E = int(rng.choice([16, 32, 64])); dtype = "bf16"
+            d = 256 * int(rng.integers(1, 3)); F = 256 * int(rng.integers(1, 3)); Fs = 256 * int(rng.integers(0, 2))
+        G = int(rng.choice([g for g in _divisors(E) if E // g >= 2])) if sigmoid else 1
+        M = int(rng.integers(1, G + 1))
+        k = int(rng.integers(1, min(M * (E // G), 8) + 1))
+        if kind == "small":
+            T = int(rng.integers(1, 512 // k + 1))
+        elif kind == "tiled_f32":
+            T = int(rng.integers(513 // k + 1, 600 // k + 200))
+        elif kind == "tiled_bf16":
+            T = int(rng.integers(1, 400))
+        elif kind == "stream":
+            T = int(rng.integers(-(-64 * E // k), -(-64 * E // k) + 300))
+        else:
+            T = int(rng.integers(1, max(2, 64 * E // k)))
+            T = min(T, 96)
+        w = Workload(f"random_{kind}_{i}", T, d, E, k, F, Fs, "sigmoid" if sigmoid else "softmax", G, M,
+                     2.5 if sigmoid else 1.0, dtype, "uniform" if rng.integers(0, 2) else "zero")
+        if moe.moe_plan_describe(moe.MoeConfig.from_workload(w))[0] == kinds[kind]:
+            out[w.name] = w
+    return out
+
+
+RANDOM = random_shapes()
+
+
+@pytest.mark.parametrize("name", list(RANDOM))
+def test_random_shapes_every_token(dev, name):
+    w = RANDOM[name]
+    log(f"[random] {w}")
+    inp = to_dev(make_inputs(w, seed=17, device="cpu"), dev)
+    y, idx, g = run(w, inp)
+    st = check_full(w, inp, y, idx, g)
+    log(f"[random] {name} {st}")
