@@ -35,17 +35,23 @@ __device__ __forceinline__ void fma8(float (&acc)[8], float g, const uint4 &o) {
   }
 }
 
+// One thread per 16-byte chunk of a token row: block (t, y) covers chunks
+// y * kCombineThreads .. of token t, so every thread issues all its loads
+// (Z, the k rows of O, R) before its first wait and no thread idles in a
+// partial last pass over the row.
+constexpr int kCombineThreads = 128;
+
 // KB: the layer's k when it is one of the common values (every load of a
 // chunk then goes out before the first wait); 0 for any other k, which runs
 // in batches of 8.  HZ / HR: Z / R present.  The sum order is the same in
 // every case: Z, then j = 0 .. k-1, then R.
 template <int KB, bool HZ, bool HR>
-__global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__ O,
-                                                    const uint16_t *__restrict__ Z,
-                                                    const int32_t *__restrict__ inv,
-                                                    const float *__restrict__ gates,
-                                                    int d, int k, const uint16_t *__restrict__ R,
-                                                    uint16_t *__restrict__ y) {
+__global__ __launch_bounds__(kCombineThreads) void combine_bf16(const uint16_t *__restrict__ O,
+                                                                const uint16_t *__restrict__ Z,
+                                                                const int32_t *__restrict__ inv,
+                                                                const float *__restrict__ gates,
+                                                                int d, int k, const uint16_t *__restrict__ R,
+                                                                uint16_t *__restrict__ y) {
   const int64_t t = blockIdx.x;
   const int nchunk = d / 8;
   __shared__ int pos[kMaxTopK];
@@ -55,46 +61,46 @@ __global__ __launch_bounds__(256) void combine_bf16(const uint16_t *__restrict__
     gw[threadIdx.x] = gates[t * k + threadIdx.x];
   }
   __syncthreads();
+  const int c = static_cast<int>(blockIdx.y) * kCombineThreads + static_cast<int>(threadIdx.x);
+  if (c >= nchunk) return;
   constexpr int NB = KB > 0 ? KB : 8;  // rows loaded together
-  for (int c = threadIdx.x; c < nchunk; c += 256) {
-    const int64_t col = static_cast<int64_t>(c) * 8;
-    uint4 z = {0u, 0u, 0u, 0u}, r = {0u, 0u, 0u, 0u};
-    if (HZ) z = load_once(Z + t * d + col);
-    if (HR) r = load_once(R + t * d + col);
-    float acc[8];
-    {
-      const uint32_t zw[4] = {z.x, z.y, z.z, z.w};
+  const int64_t col = static_cast<int64_t>(c) * 8;
+  uint4 z = {0u, 0u, 0u, 0u}, r = {0u, 0u, 0u, 0u};
+  if (HZ) z = load_once(Z + t * d + col);
+  if (HR) r = load_once(R + t * d + col);
+  float acc[8];
+  {
+    const uint32_t zw[4] = {z.x, z.y, z.z, z.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = bf16_to_f32(static_cast<uint16_t>(zw[i] & 0xffffu));
-        acc[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(zw[i] >> 16));
-      }
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = bf16_to_f32(static_cast<uint16_t>(zw[i] & 0xffffu));
+      acc[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(zw[i] >> 16));
     }
-    const int kk = KB > 0 ? KB : k;
-    for (int j0 = 0; j0 < kk; j0 += NB) {
-      uint4 o[NB];
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (KB > 0 || j0 + i < kk) o[i] = load_once(O + static_cast<int64_t>(pos[j0 + i]) * d + col);
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (KB > 0 || j0 + i < kk) fma8(acc, gw[j0 + i], o[i]);
-    }
-    if (HR) {  // the block's residual, added last
-      const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(rw[i] & 0xffffu));
-        acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(rw[i] >> 16));
-      }
-    }
-    uint4 out;
-    out.x = pack_bf16x2(acc[0], acc[1]);
-    out.y = pack_bf16x2(acc[2], acc[3]);
-    out.z = pack_bf16x2(acc[4], acc[5]);
-    out.w = pack_bf16x2(acc[6], acc[7]);
-    *reinterpret_cast<uint4 *>(y + t * d + col) = out;
   }
+  const int kk = KB > 0 ? KB : k;
+  for (int j0 = 0; j0 < kk; j0 += NB) {
+    uint4 o[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      if (KB > 0 || j0 + i < kk) o[i] = load_once(O + static_cast<int64_t>(pos[j0 + i]) * d + col);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      if (KB > 0 || j0 + i < kk) fma8(acc, gw[j0 + i], o[i]);
+  }
+  if (HR) {  // the block's residual, added last
+    const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(rw[i] & 0xffffu));
+      acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(rw[i] >> 16));
+    }
+  }
+  uint4 out;
+  out.x = pack_bf16x2(acc[0], acc[1]);
+  out.y = pack_bf16x2(acc[2], acc[3]);
+  out.z = pack_bf16x2(acc[4], acc[5]);
+  out.w = pack_bf16x2(acc[6], acc[7]);
+  *reinterpret_cast<uint4 *>(y + t * d + col) = out;
 }
 
 __global__ __launch_bounds__(256) void combine_f32(const float *__restrict__ O,
@@ -153,7 +159,9 @@ hipError_t launch_combine(const Plan &p, const float *gates, const void *residua
       case 8: kern = pick(std::integral_constant<int, 8>{}); break;
       default: break;
     }
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, static_cast<const uint16_t *>(p.O),
+    const unsigned ny = static_cast<unsigned>((c.d / 8 + kCombineThreads - 1) / kCombineThreads);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(c.T), ny), dim3(kCombineThreads), 0, s,
+                       static_cast<const uint16_t *>(p.O),
                        static_cast<const uint16_t *>(Z), p.inv, gates, c.d, c.k,
                        static_cast<const uint16_t *>(residual), static_cast<uint16_t *>(y));
   } else
