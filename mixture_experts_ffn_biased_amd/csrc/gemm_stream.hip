@@ -8,7 +8,7 @@
 // the schedule and the data movement differ:
 //
 //  * One workgroup per CU loops over work items (tile, n-slab).  Items are
-//    kept in eight per-XCD lists: a chunk (up to two tiles of one expert)
+//    kept in eight per-XCD lists: a chunk (up to eight tiles of one expert)
 //    goes to one XCD with all its n-slabs, the tiles of a chunk adjacent.
 //    Workgroups of an XCD take items from their list in order through an
 //    atomic counter, so the workgroups running together on an XCD share the
@@ -426,10 +426,11 @@ __device__ __forceinline__ void kloop_prefill(const PRing &ring, const PPtrs &p,
       dma16_buf(real && ((p.alive >> j) & 1) ? p.ar : none, p.ao(j), q * p.astep,
                 st + (wave * V<0>::PA_LOADS + j) * 1024);
   };
-  // A weight slab is read by at most the two tiles of its chunk, close
-  // together in time, while the gathered token rows are read again by other
-  // experts' tiles: the slab loads carry the non-temporal hint so that the
-  // weight stream does not push the token rows out of the last-level cache.
+  // A weight slab is read by the tiles of its chunk (up to eight), close
+  // together in time, while the gathered token rows are read again by the
+  // other slab items of their tile and by other experts' tiles: the slab
+  // loads carry the non-temporal hint so that the weight stream does not push
+  // the token rows out of the cache.
   auto issue_b = [&](unsigned char *st, int kt, bool real) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < V<0>::B_LOADS; ++i)
@@ -926,11 +927,14 @@ __global__ __launch_bounds__(256) void fold_rows(const uint16_t *__restrict__ W,
 // ---- schedule: per-XCD item lists ------------------------------------------
 
 constexpr int kMaxChunks = 4096;
+// Tiles of one expert a chunk holds at most.  Whole experts of up to 8 tiles
+// on one XCD: each slab is fetched once and read by all their tiles together.
+constexpr int kChunkTiles = 8;
 constexpr int kScheduleBlocks = 64;  // blocks of stream_schedule: 256 waves share out the chunks
 
 // Rebuilds the tile numbering of perm_scan (experts in order, ceil(count /
 // tile_m) tiles each, then the shared expert's tiles), groups tiles into
-// chunks of up to two per expert, deals chunks to XCDs round-robin and writes
+// chunks of up to kChunkTiles per expert, deals chunks to XCDs round-robin and writes
 // both GEMMs' item lists (tile fastest, then n-slab, within a chunk).  Every
 // block derives the same chunk table from the counts; the waves of all blocks
 // then share out the chunks, a wave writing one chunk's run of items with
@@ -950,7 +954,7 @@ __global__ __launch_bounds__(256) void stream_schedule(
   const int e = tid;
   const int c = e < E ? counts[e] : 0;
   const int nt = (c + tile_m - 1) / tile_m;
-  const int nch = (nt + 1) / 2;
+  const int nch = (nt + kChunkTiles - 1) / kChunkTiles;
   // exclusive scans of tiles and chunks
   buf[tid] = nt;
   __syncthreads();
@@ -975,16 +979,16 @@ __global__ __launch_bounds__(256) void stream_schedule(
   const int routed_chunks = buf[255];
   __syncthreads();
   for (int j = 0; j < nch; ++j) {
-    cfirst[chunk_off + j] = tile_off + 2 * j;
-    cmt[chunk_off + j] = static_cast<unsigned char>(nt - 2 * j < 2 ? nt - 2 * j : 2);
+    cfirst[chunk_off + j] = tile_off + kChunkTiles * j;
+    cmt[chunk_off + j] = static_cast<unsigned char>(nt - kChunkTiles * j < kChunkTiles ? nt - kChunkTiles * j : kChunkTiles);
   }
   int n_chunks = routed_chunks;
   if (has_shared) {
     const int ns = static_cast<int>((T + tile_m - 1) / tile_m);
-    const int nsc = (ns + 1) / 2;
+    const int nsc = (ns + kChunkTiles - 1) / kChunkTiles;
     for (int j = tid; j < nsc; j += 256) {
-      cfirst[routed_chunks + j] = routed_tiles + 2 * j;
-      cmt[routed_chunks + j] = static_cast<unsigned char>(ns - 2 * j < 2 ? ns - 2 * j : 2);
+      cfirst[routed_chunks + j] = routed_tiles + kChunkTiles * j;
+      cmt[routed_chunks + j] = static_cast<unsigned char>(ns - kChunkTiles * j < kChunkTiles ? ns - kChunkTiles * j : kChunkTiles);
     }
     n_chunks += nsc;
   }
@@ -1025,7 +1029,7 @@ __global__ __launch_bounds__(256) void stream_schedule(
       const int ntl = list == 0 ? (sh ? nt_gu_s : nt_gu_r) : (sh ? nt_dn_s : nt_dn_r);
       int2 *out = (list == 0 ? items_gu : items_dn) + xoff[list][ch & 7] + cpos[list][ch];
       for (int q = lane; q < ntl * mt; q += 64)
-        out[q] = mt == 2 ? make_int2(first + (q & 1), q >> 1) : make_int2(first, q);
+        out[q] = make_int2(first + q % mt, q / mt);
     }
   }
 }
@@ -1061,8 +1065,8 @@ StreamArgs base_args(const Plan &p, int list) {
 
 int stream_tile_m(int path) { return path == PATH_STREAM_DECODE ? V<1>::BM : V<0>::BM; }
 // Prefill tiles of one expert get equal row counts (same tile count), so the
-// two tiles of a chunk, which share its weight slabs, run for the same time
-// and read each slab together.
+// tiles of a chunk, which share its weight slabs, run for the same time and
+// read each slab together.
 int stream_tile_balanced(int path) { return path == PATH_STREAM ? 1 : 0; }
 int stream_max_chunks() { return kMaxChunks; }
 // Gated bodies: 128 columns of W1 and W3 a slab; the GELU MLP: 256 of W1.
