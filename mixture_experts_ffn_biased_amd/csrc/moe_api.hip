@@ -60,6 +60,8 @@ static int choose_path(const moe_cfg &c, int kind) {
   // matrix with 32-bit byte offsets from their starts.
   const int64_t f_max = c.F > c.F_shared ? c.F : c.F_shared;
   if (path == PATH_STREAM && (c.T * c.d * 2 >= (1LL << 32) || f_max * c.d * 2 >= (1LL << 32))) return PATH_TILED;
+  // A conservative bound on the schedule's chunks (the count chunks of at
+  // most two tiles would reach; larger chunks make fewer).
   const int64_t m = stream_tile_m(path);
   const int64_t chunks = S / (2 * m) + c.E + c.T / (2 * m) + 4;
   if (chunks > stream_max_chunks()) return PATH_TILED;
